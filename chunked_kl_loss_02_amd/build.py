@@ -1,0 +1,52 @@
+"""Compiles libkdkl.so (the HIP kernels and the C ABI) for gfx950, in-tree.
+
+    python -m chunked_kl_loss_02_amd.build
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+LIB = os.path.join(HERE, "libkdkl.so")
+SOURCES = [os.path.join(CSRC, "kd_host.hip")]
+DEPS = SOURCES + [os.path.join(CSRC, f) for f in ("kd_common.hpp", "kd_gemm.hpp", "kd_kernels.hpp")] + [
+    os.path.join(os.path.dirname(HERE), "include", "kdkl.h")]
+
+ARCH = "gfx950"
+
+
+def hipcc() -> str:
+    for c in (shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
+        if c and os.path.exists(c):
+            return c
+    raise RuntimeError("hipcc not found")
+
+
+def command(out: str = LIB) -> list:
+    return [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+            # packed fp32 VALU ops stay disabled: scalar fp32 only
+            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-Wno-unused-result", *SOURCES, "-o", out]
+
+
+def build(verbose: bool = False) -> str:
+    """Always recompiles; writes via a temporary file so a concurrent reader
+    never sees a half-written library."""
+    tmp = LIB + ".tmp"
+    cmd = command(tmp)
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError(f"hipcc failed with exit code {r.returncode}")
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

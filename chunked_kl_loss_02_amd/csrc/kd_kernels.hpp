@@ -1,0 +1,437 @@
+// gfx950 kernels of the fused chunked top-K KL distillation loss.
+//
+// The loss (page "Efficient Knowledge Distillation for LLMs: Offline Top-K
+// Logits and a Fused Chunked KL Loss", abstract; page "Making Knowledge
+// Distillation Cheap Enough to Run at Scale", section "Two systems changes"):
+// the student's logits S = h W^T are projected one block at a time, folded
+// into a running log-sum-exp per token and discarded; the teacher is its
+// cached top-K logits, renormalised over those K entries; the backward pass
+// recomputes each block.  With c = log2(e)/tau all exponentials run in base 2.
+//
+//   pass 1 : k_pass1   S^T tile = W_tile h_tile^T (MFMA), per token running
+//                      (max, sum 2^(c S - max)) over its vocabulary range
+//            k_lse     merges the per-range partials -> lse2[t] (log2 units)
+//   teacher: k_teacher p = softmax_K(u/tau), merged mass of duplicate ids,
+//                      sum_k p log(mass) per row; k_gather s[t,k] = S[t, idx]
+//   loss   : k_rows / k_sum   KL_t = sum p log p - sum p s / tau + LSE_t
+//   pass 2 : k_pass2   recomputes the S^T tile, writes the logit gradient
+//                      G = coef * 2^(c S - lse2) (bf16) for one (token block,
+//                      vocabulary chunk); k_fixup subtracts the teacher mass
+//                      at the cached ids; k_bwd contracts G into dH (over the
+//                      chunk's vocabulary) and dW (over the block's tokens).
+#pragma once
+#include "kd_gemm.hpp"
+
+namespace kd {
+
+// ----------------------------------------------------------------- small ops
+__global__ void __launch_bounds__(1024) k_count(const uint8_t* __restrict__ mask, int64_t T, float tau,
+                                                float* __restrict__ scal_f, int64_t* __restrict__ scal_i) {
+  __shared__ int64_t part[1024];
+  int64_t c = 0;
+  for (int64_t t = threadIdx.x; t < T; t += 1024) c += mask ? (mask[t] != 0) : 1;
+  part[threadIdx.x] = c;
+  __syncthreads();
+  for (int s = 512; s > 0; s >>= 1) {
+    if ((int)threadIdx.x < s) part[threadIdx.x] += part[threadIdx.x + s];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const int64_t N = part[0];
+    scal_i[0] = N;
+    scal_f[0] = N > 0 ? (float)(1.0 / ((double)N * (double)tau)) : 0.0f;  // gradient coefficient
+    scal_f[1] = N > 0 ? (float)(1.0 / (double)N) : 0.0f;
+  }
+}
+
+__global__ void k_fill(float* __restrict__ p, int64_t n, float v) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) p[i] = v;
+}
+
+// (m, l) <- (m, l) merged with (om, ol), l = sum 2^(x - m); (-inf, 0) is empty.
+__device__ __forceinline__ void lse_merge(float& m, float& l, float om, float ol) {
+  const float nm = fmaxf(m, om);
+  if (nm == -INFINITY) return;
+  l = l * fast_exp2(m - nm) + ol * fast_exp2(om - nm);
+  m = nm;
+}
+
+// Teacher side, one wave per token: p = softmax over the K cached logits at
+// temperature tau; pm[k] = total mass on id idx[k] (duplicates add);
+// negent[t] = sum_k p_k log pm_k (= sum_v P log P on the vocabulary).
+constexpr int kTeacherMaxK = 1024;
+__global__ void __launch_bounds__(256) k_teacher(const int32_t* __restrict__ idx, const float* __restrict__ logit,
+                                                 const uint8_t* __restrict__ mask, int64_t T, int K, int64_t V,
+                                                 float inv_tau, float* __restrict__ p_out, float* __restrict__ pm_out,
+                                                 float* __restrict__ negent, uint32_t* __restrict__ status, int validate) {
+  __shared__ int32_t sid[4][kTeacherMaxK];
+  __shared__ float sp[4][kTeacherMaxK];
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + w;
+  if (t >= T) return;
+  const int32_t* ir = idx + t * K;
+  const float* lr = logit + t * K;
+  float* pr = p_out + t * K;
+  float* pmr = pm_out + t * K;
+  const bool keep = mask ? mask[t] != 0 : true;
+  if (!keep) {
+    for (int k = lane; k < K; k += 64) { pr[k] = 0.f; pmr[k] = 0.f; }
+    if (lane == 0) negent[t] = 0.f;
+    return;
+  }
+  float mx = -INFINITY;
+  uint32_t bad = 0;
+  for (int k = lane; k < K; k += 64) {
+    const float u = lr[k] * inv_tau;
+    mx = fmaxf(mx, u);
+    if (validate) {
+      const int32_t v = ir[k];
+      if (v < 0 || (int64_t)v >= V) bad |= 1u;
+      if (__builtin_isnan(lr[k]) || lr[k] == INFINITY) bad |= 2u;
+    }
+  }
+  mx = wave_max(mx);
+  if (validate) {
+    if (mx == -INFINITY) bad |= 2u;
+    if (bad) atomicOr(status, bad);
+  }
+  float z = 0.f;
+  for (int k = lane; k < K; k += 64) z += expf(lr[k] * inv_tau - mx);
+  z = wave_sum(z);
+  const float iz = 1.0f / z;
+  for (int k = lane; k < K; k += 64) {
+    const float p = expf(lr[k] * inv_tau - mx) * iz;
+    pr[k] = p;
+    sp[w][k] = p;
+    sid[w][k] = ir[k];
+  }
+  // make this wave's LDS writes visible to its other lanes
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+  __builtin_amdgcn_wave_barrier();
+  float ne = 0.f;
+  for (int k = lane; k < K; k += 64) {
+    const int32_t v = sid[w][k];
+    float m = 0.f;
+    for (int j = 0; j < K; ++j) m += (sid[w][j] == v) ? sp[w][j] : 0.f;
+    pmr[k] = m;
+    const float p = sp[w][k];
+    if (p > 0.f) ne += p * logf(m);
+  }
+  ne = wave_sum(ne);
+  if (lane == 0) negent[t] = ne;
+}
+
+// s[t,k] = <h[t,:], W[idx[t,k],:]> in fp32 (the student logit at each cached
+// teacher id).  One block per token, one wave per cached entry at a time.
+__global__ void __launch_bounds__(256) k_gather(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W,
+                                                const int32_t* __restrict__ idx, const uint8_t* __restrict__ mask,
+                                                int64_t T, int64_t H, int64_t V, int K, float* __restrict__ s_out) {
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t t = blockIdx.x;
+  if (t >= T) return;
+  const bool keep = mask ? mask[t] != 0 : true;
+  const __amdgpu_buffer_rsrc_t rh = make_rsrc(h + t * H, (uint64_t)H * 2);
+  const int nvec = (int)(H >> 3);
+  for (int k = w; k < K; k += 4) {
+    const int32_t v = __builtin_amdgcn_readfirstlane(idx[t * K + k]);
+    float acc = 0.f;
+    if (keep && v >= 0 && (int64_t)v < V) {
+      const __amdgpu_buffer_rsrc_t rw = make_rsrc(W + (int64_t)v * H, (uint64_t)H * 2);
+      for (int j = lane; j < nvec; j += 64) {
+        const u32x4 a = buf_load16(rh, (uint32_t)j * 16u);
+        const u32x4 b = buf_load16(rw, (uint32_t)j * 16u);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          acc = fmaf(bf16_to_f32(a[q] & 0xFFFFu), bf16_to_f32(b[q] & 0xFFFFu), acc);
+          acc = fmaf(bf16_to_f32(a[q] >> 16), bf16_to_f32(b[q] >> 16), acc);
+        }
+      }
+    }
+    acc = wave_sum(acc);
+    if (lane == 0) s_out[t * K + k] = acc;
+  }
+}
+
+// ----------------------------------------------------------------- pass 1
+// Grid: padded to a multiple of 8; work id -> (token tile, vocabulary range).
+// Each workgroup walks `per` vocabulary tiles of 256 for one token tile of
+// 256 and writes one (max, sum) pair per token for its range:
+//   part[range * ldp + t] = (m, l) with l = sum_v 2^(c S[t,v] - m).
+struct Pass1Args {
+  const uint16_t* W;     // [V, H]
+  const uint16_t* h;     // token block origin [rows, H]
+  float2* part;          // [nranges, ldp]
+  int64_t V, H, rows;    // rows = valid tokens in the block
+  int ntt, nvt, per, nranges, gt, total, ldp;
+  float c;               // log2(e) / tau
+};
+
+__global__ void __launch_bounds__(256, 1) k_pass1(Pass1Args a) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * 512 * kBK];
+  __shared__ float2 red[2][128];
+  const int id = xcd_remap(blockIdx.x, gridDim.x);
+  if (id >= a.total) return;
+  int tt, vr;
+  grouped(id, a.ntt, a.nranges, a.gt, tt, vr);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int wm = w & 1, wn = w >> 1;
+  const int nk = (int)(a.H / kBK);
+  const int vt0 = vr * a.per, vt1 = min(a.nvt, vt0 + a.per);
+
+  LoaderKC<256> lb;
+  lb.init(a.h + (int64_t)tt * 256 * a.H, a.rows - (int64_t)tt * 256, a.H);
+  float rm[4], rl[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) { rm[j] = -INFINITY; rl[j] = 0.f; }
+  f32x16 acc[4][4];
+  for (int vt = vt0; vt < vt1; ++vt) {
+    LoaderKC<256> la;
+    la.init(a.W + (int64_t)vt * 256 * a.H, a.V - (int64_t)vt * 256, a.H);
+    gemm_tile<4, 4>(la, lb, nk, lds, acc);
+    // vocabulary rows of this lane: vt*256 + wm*128 + acc_row(i, e)
+    const int64_t vbase = (int64_t)vt * 256 + wm * 128;
+    const bool ragged = vbase + 128 > a.V;
+    if (ragged) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          if (vbase + acc_row(i, e, lane) >= a.V)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[i][j][e] = -INFINITY;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, acc[i][j][e]);
+      const float nm = fmaxf(rm[j], mx * a.c);
+      const float ref = nm == -INFINITY ? 0.f : nm;  // rows of this lane all past V
+      float sum = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sum += fast_exp2(fmaf(acc[i][j][e], a.c, -ref));
+      rl[j] = rl[j] * fast_exp2(rm[j] - ref) + sum;
+      rm[j] = nm;
+    }
+  }
+  // merge the two lane halves (same token, other vocabulary rows)
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float om = __shfl_xor(rm[j], 32, 64);
+    const float ol = __shfl_xor(rl[j], 32, 64);
+    lse_merge(rm[j], rl[j], om, ol);
+  }
+  // merge the two M waves through LDS
+  if (wm == 1 && lane < 32) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) red[wn][acc_col(j, lane)] = make_float2(rm[j], rl[j]);
+  }
+  __syncthreads();
+  if (wm == 0 && lane < 32) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float2 o = red[wn][acc_col(j, lane)];
+      lse_merge(rm[j], rl[j], o.x, o.y);
+      const int t = tt * 256 + wn * 128 + acc_col(j, lane);
+      a.part[(int64_t)vr * a.ldp + t] = make_float2(rm[j], rl[j]);
+    }
+  }
+}
+
+// lse2[t] = log2 sum_v 2^(c S[t,v]) from the per-range partials (fixed order).
+__global__ void k_lse(const float2* __restrict__ part, int nranges, int ldp, int64_t rows,
+                      float* __restrict__ lse2) {
+  const int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (t >= rows) return;
+  float m = -INFINITY, l = 0.f;
+  for (int r = 0; r < nranges; ++r) {
+    const float2 p = part[(int64_t)r * ldp + t];
+    lse_merge(m, l, p.x, p.y);
+  }
+  lse2[t] = m + log2f(l);
+}
+
+// Per-row KL and per-block partial sums (fp64, fixed order).
+__global__ void __launch_bounds__(256) k_rows(const float* __restrict__ p, const float* __restrict__ s,
+                                              const float* __restrict__ negent, const float* __restrict__ lse2,
+                                              const uint8_t* __restrict__ mask, int64_t T, int K, float inv_tau,
+                                              float* __restrict__ row_loss, double* __restrict__ bsum) {
+  __shared__ double red[256];
+  const int64_t t = blockIdx.x * (int64_t)256 + threadIdx.x;
+  double v = 0.0;
+  if (t < T && (mask ? mask[t] != 0 : true)) {
+    float g = 0.f;
+    for (int k = 0; k < K; ++k) g = fmaf(p[t * K + k], s[t * K + k], g);
+    v = (double)negent[t] - (double)g * (double)inv_tau + (double)lse2[t] * (double)kLn2;
+  }
+  if (t < T) row_loss[t] = (float)v;
+  red[threadIdx.x] = v;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if ((int)threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) bsum[blockIdx.x] = red[0];
+}
+
+__global__ void __launch_bounds__(1024) k_sum(const double* __restrict__ bsum, int64_t nb,
+                                              const float* __restrict__ scal_f, float* __restrict__ loss) {
+  __shared__ double red[1024];
+  double v = 0.0;
+  for (int64_t i = threadIdx.x; i < nb; i += 1024) v += bsum[i];
+  red[threadIdx.x] = v;
+  __syncthreads();
+  for (int o = 512; o > 0; o >>= 1) {
+    if ((int)threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) loss[0] = (float)(red[0] * (double)scal_f[1]);
+}
+
+// ----------------------------------------------------------------- pass 2
+// One (token block, vocabulary chunk): G[t, v] = coef_t 2^(c S[t,v] - lse2[t])
+// in bf16 for every (t, v) of the padded tile grid (zero outside the valid
+// range or on masked tokens).
+struct Pass2Args {
+  const uint16_t* W;      // chunk origin [V - v0, H]
+  const uint16_t* h;      // block origin
+  const float* lse2;      // block origin
+  const uint8_t* mask;    // block origin (nullable)
+  const float* scal_f;
+  uint16_t* G;            // [ntt*256, ldg]
+  int64_t vrows, H, rows; // valid vocabulary rows in chunk / tokens in block
+  int ntt, nvt, gt, total, ldg;
+  float c;
+};
+
+__global__ void __launch_bounds__(256, 1) k_pass2(Pass2Args a) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * 512 * kBK];
+  const int id = xcd_remap(blockIdx.x, gridDim.x);
+  if (id >= a.total) return;
+  int tt, vt;
+  grouped(id, a.ntt, a.nvt, a.gt, tt, vt);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int wm = w & 1, wn = w >> 1;
+  LoaderKC<256> la, lb;
+  la.init(a.W + (int64_t)vt * 256 * a.H, a.vrows - (int64_t)vt * 256, a.H);
+  lb.init(a.h + (int64_t)tt * 256 * a.H, a.rows - (int64_t)tt * 256, a.H);
+  f32x16 acc[4][4];
+  gemm_tile<4, 4>(la, lb, (int)(a.H / kBK), lds, acc);
+  const float coef = a.scal_f[0];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int t = tt * 256 + wn * 128 + acc_col(j, lane);
+    const bool tv = t < a.rows && (a.mask ? a.mask[t] != 0 : true);
+    const float l2 = tv ? a.lse2[t] : 0.f;
+    const float cf = tv ? coef : 0.f;
+    uint16_t* grow = a.G + (int64_t)t * a.ldg;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int vl = vt * 256 + wm * 128 + acc_row(i, 4 * q, lane);  // 4 consecutive rows
+        float g[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float x = cf * fast_exp2(fmaf(acc[i][j][4 * q + r], a.c, -l2));
+          g[r] = (vl + r < a.vrows) ? x : 0.f;
+        }
+        u32x2 pk;
+        pk[0] = pack_bf16x2(g[0], g[1]);
+        pk[1] = pack_bf16x2(g[2], g[3]);
+        *reinterpret_cast<u32x2*>(grow + vl) = pk;
+      }
+  }
+}
+
+// At each cached teacher id inside this (block, chunk), replace the dense
+// value by coef * (q - mass) with q = 2^(c s - lse2) from the gathered logit.
+__global__ void k_fixup(const int32_t* __restrict__ idx, const float* __restrict__ s, const float* __restrict__ pm,
+                        const float* __restrict__ lse2, const uint8_t* __restrict__ mask,
+                        const float* __restrict__ scal_f, int64_t rows, int K, int64_t v0, int64_t vrows, float c,
+                        uint16_t* __restrict__ G, int ldg) {
+  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (i >= rows * K) return;
+  const int64_t t = i / K;
+  if (mask && mask[t] == 0) return;
+  const int64_t v = (int64_t)idx[i] - v0;
+  if (v < 0 || v >= vrows) return;
+  const float q = fast_exp2(fmaf(s[i], c, -lse2[t]));
+  const float g = scal_f[0] * (q - pm[i]);
+  G[t * ldg + v] = __builtin_bit_cast(uint16_t, (__bf16)g);
+}
+
+// dH (over the chunk's vocabulary) and dW (over the block's tokens) from G.
+// Work ids [0, ndh) are dH tiles (hidden tile x token tile, K = vocabulary);
+// the rest are dW tiles (hidden tile x vocabulary tile, K = tokens).  Both
+// are computed transposed so that a lane stores 4 consecutive hidden units.
+struct BwdArgs {
+  const uint16_t* W;      // chunk origin
+  const uint16_t* h;      // block origin
+  const uint16_t* G;      // [*, ldg]
+  float* dH;              // block origin [rows, H] (nullable)
+  float* dW;              // chunk origin [vrows, H] (nullable)
+  int64_t vrows, H, rows; // valid rows
+  int nht, ntt, nvt, ndh, ndw, ldg, grows;  // grows = allocated rows of G
+  int acc_dh, acc_dw;     // accumulate (1) or overwrite (0)
+};
+
+__global__ void __launch_bounds__(256, 1) k_bwd(BwdArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * 512 * kBK];
+  const int id = blockIdx.x;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int wm = w & 1, wn = w >> 1;
+  f32x16 acc[4][4];
+  float* out;
+  int64_t nvalid;
+  int mt, nt, acc_mode;
+  if (id < a.ndh) {
+    mt = id % a.nht;
+    nt = id / a.nht;
+    // A(m = hidden, k = vocab) = W[v, m]: row-contiguous; B(k = vocab, n = token) = G[n, v]: k-contiguous
+    LoaderRC<256> la;
+    LoaderKC<256> lb;
+    la.init(a.W, a.vrows, a.H, mt * 256);
+    lb.init(a.G + (int64_t)nt * 256 * a.ldg, (int64_t)a.grows - (int64_t)nt * 256, a.ldg);
+    gemm_tile<4, 4>(la, lb, (int)((a.vrows + kBK - 1) / kBK), lds, acc);
+    out = a.dH;
+    nvalid = a.rows;
+    acc_mode = a.acc_dh;
+  } else {
+    const int j = id - a.ndh;
+    mt = j % a.nht;
+    nt = j / a.nht;
+    // A(m = hidden, k = token) = h[t, m]; B(k = token, n = vocab) = G[t, n]: both row-contiguous
+    LoaderRC<256> la;
+    LoaderRC<256> lb;
+    la.init(a.h, a.rows, a.H, mt * 256);
+    lb.init(a.G, a.grows, a.ldg, nt * 256);
+    gemm_tile<4, 4>(la, lb, (int)((a.rows + kBK - 1) / kBK), lds, acc);
+    out = a.dW;
+    nvalid = a.vrows;
+    acc_mode = a.acc_dw;
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t n = (int64_t)nt * 256 + wn * 128 + acc_col(j, lane);
+    if (n >= nvalid) continue;
+    float* orow = out + n * a.H;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t m = (int64_t)mt * 256 + wm * 128 + acc_row(i, 4 * q, lane);
+        if (m >= a.H) continue;
+        f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+        f32x4* dst = reinterpret_cast<f32x4*>(orow + m);
+        if (acc_mode) v += *dst;
+        *dst = v;
+      }
+  }
+}
+
+}  // namespace kd

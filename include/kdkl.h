@@ -1,0 +1,126 @@
+/* kdkl.h — C ABI of the fused chunked top-K KL distillation loss (MI355X / gfx950).
+ *
+ * What it computes.  The pages "Efficient Knowledge Distillation for LLMs:
+ * Offline Top-K Logits and a Fused Chunked KL Loss" (abstract) and "Making
+ * Knowledge Distillation Cheap Enough to Run at Scale" (section "Two systems
+ * changes") describe a KL-divergence distillation loss whose student side is
+ * the output projection of hidden states h[T,H] through the head weight
+ * W[V,H], and whose teacher side is an offline cache of the teacher's top-K
+ * logits per position.  The fused variant projects, reduces and discards one
+ * chunk of logits at a time and recomputes each chunk in the backward pass,
+ * so the T x V logit tensor is never stored.  With the readings this library
+ * adopts (tau divides both sides, no tau^2 factor, mean over kept tokens):
+ *
+ *   q[t,v]  = softmax_v(S[t,:]/tau),  S = h W^T          (full vocabulary)
+ *   p[t,k]  = softmax_k(teacher_logit[t,k]/tau)          (renormalised over K)
+ *   P[t,v]  = sum_k p[t,k] [teacher_idx[t,k] == v]        (duplicates add)
+ *   KL_t    = sum_v P[t,v] (log P[t,v] - log q[t,v])      (0 log 0 = 0)
+ *   loss    = (1/N) sum_t mask_t KL_t,  N = sum_t mask_t  (loss = 0 if N = 0)
+ *   dH      = G W,  dW = G^T h,  G[t,v] = mask_t (q[t,v] - P[t,v]) / (N tau)
+ *
+ * Precision: bf16 h and W, fp32 MFMA accumulation, fp32 exponentials and
+ * logarithms, the logit gradient rounded once to bf16 (round to nearest
+ * even) before the two gradient contractions, fp32 dH and dW.
+ *
+ * Memory: besides the caller's inputs and outputs the library touches only
+ * the caller's workspace (see kd_topk_kl_workspace_size): a fixed
+ * block_t x chunk_v bf16 gradient buffer plus O(T*K + T*V/(256*per)) per-token
+ * state.  It allocates no device memory, keeps no state between calls (except
+ * the optional timing facility below) and is reentrant across streams given
+ * distinct workspaces.
+ */
+#ifndef KDKL_H
+#define KDKL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum kd_status {
+  KD_OK = 0,
+  KD_ERR_ARG = 1,          /* invalid argument (null pointer, bad size, tau <= 0 ...) */
+  KD_ERR_UNSUPPORTED = 2,  /* valid but not supported: H % 64 != 0, K > 1024, bad alignment */
+  KD_ERR_WORKSPACE = 3,    /* workspace_bytes smaller than kd_topk_kl_workspace_size() */
+  KD_ERR_INDEX = 4,        /* (KD_FLAG_VALIDATE) a kept row has a teacher id outside [0, V) */
+  KD_ERR_NONFINITE = 5,    /* (KD_FLAG_VALIDATE) a kept row has a NaN/+inf logit or all -inf */
+  KD_ERR_HIP = 6           /* a HIP runtime call failed (no device, launch failure ...) */
+} kd_status;
+
+/* Check teacher ids and logits of kept rows on the device, then synchronise
+ * the stream and report KD_ERR_INDEX / KD_ERR_NONFINITE.  Without this flag
+ * valid inputs are a precondition (out-of-range ids never fault: they read
+ * zeros and give meaningless results). */
+#define KD_FLAG_VALIDATE 1u
+
+typedef struct kd_problem {
+  int64_t T;        /* tokens (rows of h); 0 allowed (loss = 0, dW = 0) */
+  int64_t H;        /* hidden size; multiple of 64 */
+  int64_t V;        /* vocabulary size; >= 1 */
+  int32_t K;        /* cached teacher entries per token; 1 <= K <= min(V, 1024) */
+  float tau;        /* temperature; finite, > 0 */
+  int32_t chunk_v;  /* vocabulary chunk of the gradient pass; 0 = 16384; multiple of 256 */
+  int32_t block_t;  /* token block of both passes; 0 = 16384; multiple of 256 */
+  uint32_t flags;   /* KD_FLAG_* */
+} kd_problem;
+
+/* Bytes of device workspace kd_topk_kl_fwd_bwd needs for this problem.
+ * Synchronous, host only; returns KD_ERR_ARG / KD_ERR_UNSUPPORTED for a
+ * problem the main call would reject. */
+kd_status kd_topk_kl_workspace_size(const kd_problem* p, size_t* bytes);
+
+/* Forward and backward of the loss above, enqueued on `stream`.
+ *
+ *   h             [T,H]  bf16 bit patterns, row-major, device, 16-byte aligned
+ *   W             [V,H]  bf16 bit patterns, row-major, device, 16-byte aligned
+ *   teacher_idx   [T,K]  int32 vocabulary ids, row-major, device
+ *   teacher_logit [T,K]  fp32 cached teacher logits (any per-row shift; -inf = no mass)
+ *   mask          [T]    uint8, nonzero = token counts; NULL = all tokens count
+ *   loss          [1]    fp32, device, overwritten
+ *   dH            [T,H]  fp32, device, 16-byte aligned, overwritten; NULL = not computed
+ *   dW            [V,H]  fp32, device, 16-byte aligned, overwritten; NULL = not computed
+ *   row_loss      [T]    fp32 mask_t * KL_t (not divided by N), device; NULL = not written
+ *   workspace     device memory of at least kd_topk_kl_workspace_size() bytes,
+ *                 256-byte aligned; contents on entry are irrelevant
+ *   stream        hipStream_t (NULL = the null stream)
+ *
+ * All pointers are borrowed: the caller owns every buffer, which must stay
+ * valid until the stream reaches this call's end.  Argument errors are
+ * returned synchronously before anything is enqueued; otherwise the call
+ * returns KD_OK as soon as the work is enqueued (KD_FLAG_VALIDATE: after it
+ * has finished).  With dH = dW = NULL only the loss pass runs. */
+kd_status kd_topk_kl_fwd_bwd(const kd_problem* p,
+                             const uint16_t* h, const uint16_t* W,
+                             const int32_t* teacher_idx, const float* teacher_logit,
+                             const uint8_t* mask,
+                             float* loss, float* dH, float* dW, float* row_loss,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* Device address, inside a workspace used by the last completed call with
+ * problem p, of the per-token log-sum-exp of S/tau (natural log would be
+ * value * ln 2: the array holds log2 of sum_v 2^(log2(e) S[t,v]/tau), fp32,
+ * [T]).  NULL if p is invalid. */
+const float* kd_topk_kl_workspace_lse2(const kd_problem* p, const void* workspace);
+
+/* Static message for a status code. */
+const char* kd_status_string(kd_status s);
+
+/* ABI version (incremented on any change of the declarations above). */
+int kd_abi_version(void);
+
+/* Optional per-kernel timing with HIP events recorded on the launch stream
+ * around every launch of the library's kernels while enabled.  Intended for
+ * benchmarks; not thread-safe.  Kernel classes: 0 teacher, 1 gather,
+ * 2 pass1, 3 lse, 4 loss, 5 pass2, 6 fixup, 7 bwd, 8 other.
+ * kd_timing_collect synchronises the recorded events, adds each class's
+ * elapsed milliseconds and launch count to ms[9] / launches[9] (either may be
+ * NULL) and releases the events. */
+kd_status kd_timing_enable(int on);
+kd_status kd_timing_collect(double* ms, int64_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KDKL_H */

@@ -1,0 +1,115 @@
+"""C-ABI checks that need the built library but no GPU: every function that
+include/kdkl.h declares is exported, the workspace planner, and argument
+validation (which returns before any HIP call)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import chunked_kl_loss_02_amd as kd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kdkl.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(kd.library_path),
+                                reason="libkdkl.so not built (run __graft_entry__.build())")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(kd_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("kd_topk_kl_fwd_bwd", "kd_topk_kl_workspace_size", "kd_status_string"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", kd.library_path], capture_output=True, text=True).stdout
+    exported = set(l.split()[-1] for l in out.splitlines() if l.strip())
+    missing = [n for n in declared_functions() if n not in exported]
+    assert not missing, missing
+    L = kd.lib()
+    for n in declared_functions():
+        assert hasattr(L, n)
+    assert L.kd_abi_version() == 1
+
+
+def _ws(T, H, V, K, tau=1.0, chunk_v=0, block_t=0):
+    p = kd.problem(T, H, V, K, tau, chunk_v, block_t)
+    n = ctypes.c_size_t(0)
+    code = kd.lib().kd_topk_kl_workspace_size(ctypes.byref(p), ctypes.byref(n))
+    return code, n.value
+
+
+def test_workspace_plan():
+    code, n = _ws(4096, 2880, 201088, 64)
+    assert code == 0
+    # fixed gradient buffer (4096 x 16384 bf16 = 128 MiB) plus per-token state
+    assert 128 << 20 <= n < (128 << 20) + 4096 * 8 * 1024
+    # per-token growth is linear once T exceeds one block
+    _, a = _ws(65536, 2880, 201088, 64)
+    _, b = _ws(131072, 2880, 201088, 64)
+    _, c = _ws(262144, 2880, 201088, 64)
+    assert abs((c - b) - 2 * (b - a)) <= 4096
+    assert (c - b) / 131072 < 1024  # bytes per token of workspace, far below 2V = 402 KB
+
+
+@pytest.mark.parametrize("args,code", [
+    ((4096, 2880, 201088, 64, 0.0), 1),          # tau <= 0
+    ((4096, 2880, 201088, 64, float("nan")), 1),
+    ((4096, 2880, 201088, 64, float("inf")), 1),
+    ((4096, 2880, 201088, 0, 1.0), 1),           # K = 0
+    ((4096, 2880, 50, 64, 1.0), 1),              # K > V
+    ((-1, 2880, 201088, 64, 1.0), 1),            # T < 0
+    ((4096, 2900, 201088, 64, 1.0), 2),          # H % 64
+    ((4096, 2880, 201088, 2000, 1.0), 2),        # K > 1024
+    ((0, 2880, 201088, 64, 1.0), 0),             # T = 0 is fine
+])
+def test_workspace_size_validation(args, code):
+    assert _ws(*args)[0] == code
+
+
+def test_chunk_and_block_must_be_multiples_of_256():
+    assert _ws(1000, 128, 5000, 8, 1.0, 300, 0)[0] == 2
+    assert _ws(1000, 128, 5000, 8, 1.0, 0, 100)[0] == 2
+    assert _ws(1000, 128, 5000, 8, 1.0, 512, 768)[0] == 0
+
+
+def test_fwd_bwd_rejects_bad_arguments_before_any_hip_call():
+    L = kd.lib()
+    vp = ctypes.c_void_p
+    p = kd.problem(16, 64, 100, 4)
+    fake = vp(1 << 20)  # never dereferenced: validation fails first
+    # null W
+    assert L.kd_topk_kl_fwd_bwd(ctypes.byref(p), fake, vp(0), fake, fake, vp(0), fake, vp(0), vp(0), vp(0),
+                                fake, ctypes.c_size_t(1 << 30), vp(0)) == 1
+    # misaligned h
+    assert L.kd_topk_kl_fwd_bwd(ctypes.byref(p), vp((1 << 20) + 2), fake, fake, fake, vp(0), fake, vp(0), vp(0),
+                                vp(0), fake, ctypes.c_size_t(1 << 30), vp(0)) == 2
+    # workspace too small
+    assert L.kd_topk_kl_fwd_bwd(ctypes.byref(p), fake, fake, fake, fake, vp(0), fake, vp(0), vp(0), vp(0),
+                                fake, ctypes.c_size_t(16), vp(0)) == 3
+    # bad problem
+    bad = kd.problem(16, 64, 100, 4, tau=-1.0)
+    assert L.kd_topk_kl_fwd_bwd(ctypes.byref(bad), fake, fake, fake, fake, vp(0), fake, vp(0), vp(0), vp(0),
+                                fake, ctypes.c_size_t(1 << 30), vp(0)) == 1
+
+
+def test_status_strings():
+    L = kd.lib()
+    for c in range(7):
+        assert L.kd_status_string(c)
+    assert b"workspace" in L.kd_status_string(3)
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(kd, "_lib", None)
+    monkeypatch.setattr(kd, "library_path", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError):
+        kd.lib()

@@ -1,0 +1,209 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle on
+the same seeded bf16 inputs, at sizes that span several 256-wide tiles and
+ragged edges, plus the method's degenerate cases.
+
+Tolerances: loss relative error <= 1e-3; dH and dW normwise relative error
+<= 2e-2 (bf16 inputs, fp32 accumulation, the logit gradient rounded once to
+bf16).  Outputs that must vanish are compared exactly."""
+import math
+import os
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import chunked_kl_loss_02_amd as kd
+import synth
+from oracle import kl_dense
+
+pytestmark = pytest.mark.gpu
+
+LOSS_TOL = 1e-3
+GRAD_TOL = 2e-2
+
+
+def to_dev(x, dev="cuda"):
+    h = torch.from_numpy(x["h_bits"].view(np.int16)).view(torch.bfloat16).to(dev)
+    W = torch.from_numpy(x["W_bits"].view(np.int16)).view(torch.bfloat16).to(dev)
+    idx = torch.from_numpy(np.ascontiguousarray(x["teacher_idx"], dtype=np.int32)).to(dev)
+    lg = torch.from_numpy(np.ascontiguousarray(x["teacher_logit"], dtype=np.float32)).to(dev)
+    m = torch.from_numpy(np.ascontiguousarray(x["mask"], dtype=np.uint8)).to(dev)
+    return h, W, idx, lg, m
+
+
+def nrel(a, b):
+    nb = np.linalg.norm(b)
+    return float(np.linalg.norm(a - b) / nb) if nb > 0 else float(np.linalg.norm(a))
+
+
+def run_case(x, tau, **kw):
+    print(f"[case] T={x['h'].shape[0]} H={x['h'].shape[1]} V={x['W'].shape[0]} K={x['teacher_idx'].shape[1]} "
+          f"tau={tau} {kw}", flush=True)
+    h, W, idx, lg, m = to_dev(x)
+    loss, dH, dW, rl = kd.fwd_bwd(h, W, idx, lg, m, tau, row_loss=True, **kw)
+    torch.cuda.synchronize()
+    ref = kl_dense(x["h"], x["W"], x["teacher_idx"], x["teacher_logit"], x["mask"], tau)
+    got = dict(loss=loss.item(), dH=dH.cpu().double().numpy(), dW=dW.cpu().double().numpy(),
+               row_loss=rl.cpu().double().numpy())
+    return got, ref
+
+
+def check(got, ref):
+    el = abs(got["loss"] - ref["loss"]) / max(abs(ref["loss"]), 1e-30)
+    eh = nrel(got["dH"], ref["dH"])
+    ew = nrel(got["dW"], ref["dW"])
+    er = nrel(got["row_loss"], ref["row_loss"])
+    print(f"  loss {got['loss']:.7f} ref {ref['loss']:.7f} rel {el:.2e} | dH {eh:.2e} | dW {ew:.2e} | rows {er:.2e}",
+          flush=True)
+    assert el <= LOSS_TOL
+    assert eh <= GRAD_TOL
+    assert ew <= GRAD_TOL
+    assert er <= LOSS_TOL
+
+
+def make(T, H, V, K, seed, mask="ones"):
+    return synth.make_inputs_np(T, H, V, K, seed=seed, mask=mask)
+
+
+def test_tiny_config():
+    x = make(128, 256, 4096, 32, 1)
+    got, ref = run_case(x, 1.0, chunk_v=1024)
+    check(got, ref)
+
+
+def test_ragged_everything():
+    # T < 256, H % 256 != 0, V not a multiple of 256 (last chunk and tile ragged), K = 100
+    x = make(200, 192, 4261, 100, 2)
+    x["mask"][[3, 50, 199]] = 0
+    got, ref = run_case(x, 2.0, chunk_v=1024)
+    check(got, ref)
+    assert np.all(got["dH"][[3, 50, 199]] == 0.0)
+    assert np.all(got["row_loss"][[3, 50, 199]] == 0.0)
+
+
+def test_multi_block_multi_chunk():
+    # 3 token blocks (last ragged) x 6 vocabulary chunks (last ragged)
+    x = make(700, 128, 3000, 16, 3, mask="packed8")
+    got, ref = run_case(x, 0.7, chunk_v=512, block_t=256)
+    check(got, ref)
+
+
+def test_realistic_hidden_size():
+    x = make(96, 2880, 2500, 64, 4)
+    got, ref = run_case(x, 1.0)
+    check(got, ref)
+
+
+def test_duplicates_and_neg_inf_logits():
+    x = make(64, 128, 1000, 8, 5)
+    x["teacher_idx"][0, 1] = x["teacher_idx"][0, 0]
+    x["teacher_idx"][5, :4] = x["teacher_idx"][5, 7]
+    x["teacher_logit"][9, 3:] = -np.inf
+    got, ref = run_case(x, 1.3)
+    check(got, ref)
+
+
+def test_teacher_equals_student_full_vocab():
+    # K = V and teacher logits equal to the student's (computed from the same
+    # bf16 values): KL is zero up to fp32 rounding
+    T, H, V = 64, 128, 512
+    x = make(T, H, V, 4, 6)
+    S = x["h"].astype(np.float64) @ x["W"].astype(np.float64).T
+    r = np.random.default_rng(0)
+    idx = np.stack([r.permutation(V) for _ in range(T)]).astype(np.int32)
+    x["teacher_idx"] = idx
+    x["teacher_logit"] = np.take_along_axis(S, idx.astype(np.int64), 1).astype(np.float32)
+    got, ref = run_case(x, 1.0)
+    assert abs(ref["loss"]) < 1e-6
+    assert abs(got["loss"]) < 1e-5
+    base = make(T, H, V, 16, 6)
+    gb, _ = run_case(base, 1.0)
+    assert np.linalg.norm(got["dW"]) < 1e-2 * np.linalg.norm(gb["dW"])
+
+
+def test_no_kept_tokens():
+    x = make(100, 64, 700, 4, 7)
+    x["mask"][:] = 0
+    got, ref = run_case(x, 1.0)
+    assert got["loss"] == 0.0
+    assert not np.any(got["dH"]) and not np.any(got["dW"])
+
+
+def test_single_kept_token():
+    x = make(300, 64, 700, 4, 8)
+    x["mask"][:] = 0
+    x["mask"][123] = 1
+    got, ref = run_case(x, 1.0)
+    check(got, ref)
+
+
+def test_k_equals_one_and_large_tau():
+    x = make(130, 64, 2048, 1, 9)
+    got, ref = run_case(x, 4.0)
+    check(got, ref)
+
+
+def test_empty_sequence():
+    W = torch.randn(300, 64, device="cuda").to(torch.bfloat16)
+    h = torch.empty(0, 64, device="cuda", dtype=torch.bfloat16)
+    idx = torch.empty(0, 4, device="cuda", dtype=torch.int32)
+    lg = torch.empty(0, 4, device="cuda", dtype=torch.float32)
+    loss, dH, dW = kd.fwd_bwd(h, W, idx, lg, None, 1.0)
+    torch.cuda.synchronize()
+    assert loss.item() == 0.0 and dH.numel() == 0 and not torch.any(dW)
+
+
+def test_loss_only_and_single_gradient_modes():
+    x = make(160, 128, 1500, 8, 10)
+    h, W, idx, lg, m = to_dev(x)
+    full = kd.fwd_bwd(h, W, idx, lg, m, 1.0)
+    lo = kd.fwd_bwd(h, W, idx, lg, m, 1.0, grad_h=False, grad_w=False)
+    oh = kd.fwd_bwd(h, W, idx, lg, m, 1.0, grad_w=False)
+    ow = kd.fwd_bwd(h, W, idx, lg, m, 1.0, grad_h=False)
+    torch.cuda.synchronize()
+    assert lo[0].item() == full[0].item()
+    assert torch.equal(oh[1], full[1]) and torch.equal(ow[2], full[2])
+
+
+def test_deterministic_and_chunk_invariant_loss():
+    x = make(300, 256, 5000, 16, 11)
+    h, W, idx, lg, m = to_dev(x)
+    a = kd.fwd_bwd(h, W, idx, lg, m, 1.0, chunk_v=1024)
+    b = kd.fwd_bwd(h, W, idx, lg, m, 1.0, chunk_v=1024)
+    c = kd.fwd_bwd(h, W, idx, lg, m, 1.0, chunk_v=256, block_t=256)
+    torch.cuda.synchronize()
+    for u, v in zip(a, b):
+        assert torch.equal(u, v)  # bitwise run-to-run
+    assert abs(a[0].item() - c[0].item()) <= 1e-6 * abs(a[0].item())
+    assert (torch.linalg.norm(a[2] - c[2]) / torch.linalg.norm(a[2])).item() < 1e-5
+
+
+def test_lse_matches_oracle():
+    x = make(128, 256, 4096, 32, 12)
+    h, W, idx, lg, m = to_dev(x)
+    out = kd.fwd_bwd(h, W, idx, lg, m, 1.5, return_workspace=True)
+    torch.cuda.synchronize()
+    lse = kd.lse(out[-1], 128, 256, 4096, 32, 1.5).cpu().double().numpy()
+    ref = kl_dense(x["h"], x["W"], x["teacher_idx"], x["teacher_logit"], x["mask"], 1.5, grads=False)
+    assert np.max(np.abs(lse - ref["lse"])) < 1e-4
+
+
+def test_validation_flag_reports_bad_teacher_data():
+    x = make(64, 64, 500, 4, 13)
+    h, W, idx, lg, m = to_dev(x)
+    kd.fwd_bwd(h, W, idx, lg, m, 1.0, validate=True)  # clean inputs pass
+    bad = idx.clone()
+    bad[7, 2] = 500
+    with pytest.raises(kd.KdError) as e:
+        kd.fwd_bwd(h, W, bad, lg, m, 1.0, validate=True)
+    assert e.value.code == 4
+    badl = lg.clone()
+    badl[3, 0] = float("nan")
+    with pytest.raises(kd.KdError) as e:
+        kd.fwd_bwd(h, W, idx, badl, m, 1.0, validate=True)
+    assert e.value.code == 5
+    # a masked row's teacher data is never inspected
+    m2 = m.clone()
+    m2[3] = 0
+    kd.fwd_bwd(h, W, idx, badl, m2, 1.0, validate=True)
