@@ -3,23 +3,28 @@
 // One workgroup = 256 threads = 4 wave64s arranged 2 (M) x 2 (N).  A wave
 // owns a (32*MI) x (32*NI) block of the output tile, held in MI*NI
 // v_mfma_f32_32x32x16_bf16 accumulators (16 fp32 per lane each).  K advances
-// 64 at a time through a two-stage LDS ring; global loads for step k+1 are in
-// flight while the MFMAs of step k run, so one barrier per step suffices.
+// 64 at a time through two LDS stages per operand; the loads of step k+1 are
+// in flight while the MFMAs of step k run, so one barrier per step suffices.
 //
 // Operands are loaded with raw buffer loads whose range ends exactly at the
 // last valid row: out-of-range rows read as zero, which covers the ragged
 // vocabulary, token and chunk edges without branches in the main loop.
 //
-// LDS layout of a stage: rows (M or N index) of 64 bf16 = 8 chunks of 16 B;
-// chunk c of row r lives at chunk position c ^ (r & 7) ^ ((r >> 3) & 7), so
-// the ds_read_b128 of eight consecutive rows (one MFMA operand fetch) and the
-// row-wise / transposed ds_write_b128 of the loaders hit distinct banks.
+// LDS layout of an operand stage: rows (M or N index) of 64 bf16 = 8 chunks
+// of 16 B; chunk c of row r lives at chunk position c ^ swz(r) with
+// swz(r) = (r & 7) ^ ((r >> 3) & 3).  The ds_read_b128 of 16 consecutive rows
+// (one MFMA operand fetch) then touches 16 distinct 16-byte bank groups, and
+// swz does not depend on bits >= 5 of r, so the fragment reads of the 32-row
+// subtiles of a wave differ only by an immediate offset.  The four stages
+// (A0, A1, B0, B1) are distinct LDS objects so the compiler may move the
+// loads into stage k+1 across the fragment reads of stage k.
 //
 // Two operand layouts are supported:
 //   KC : element (row, k) at base + row*ld + k   (k contiguous; e.g. W, h for S = W h^T)
 //   RC : element (row, k) at base + k*ld + row   (row contiguous; e.g. W in dH = G W)
-// RC tiles are loaded as 8x8 bf16 blocks and transposed in registers
-// (v_perm_b32) before the LDS write, so MFMA always reads k-contiguous LDS.
+// KC tiles go global -> LDS directly (buffer_load_dwordx4 ... lds); RC tiles
+// are loaded as 8x8 bf16 blocks into registers, transposed with v_perm_b32
+// and written to LDS, so the MFMAs always read k-contiguous rows.
 #pragma once
 #include "kd_common.hpp"
 
@@ -28,39 +33,49 @@ namespace kd {
 constexpr int kBK = 64;
 constexpr int kThreads = 256;
 
-__device__ __forceinline__ int lds_swz(int r) { return (r & 7) ^ ((r >> 3) & 7); }
+__device__ __forceinline__ int lds_swz(int r) { return (r & 7) ^ ((r >> 3) & 3); }
 // offset in bf16 elements of chunk `c` of row `r` in a [rows][64] stage
 __device__ __forceinline__ int lds_off(int r, int c) { return (r << 6) + ((c ^ lds_swz(r)) << 3); }
 
-// Loader for a tile of R rows x 64 k of a k-contiguous operand.
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Loader for a tile of R rows x 64 k of a k-contiguous operand, global ->
+// LDS without registers.  One wave instruction fills 8 consecutive LDS rows
+// (1 KiB, lane l at row 8q + l/8, chunk position l%8), so each lane fetches
+// the logical chunk that the swizzle maps to its slot.  Completion is
+// tracked by vmcnt.
 template <int R>
 struct LoaderKC {
-  static constexpr int NV = R / 32;  // 16-byte loads per thread
-  u32x4 v[NV];
+  static constexpr int NQ = R / 32;  // wave instructions per wave per k-step
+  static constexpr int kVmem = NQ;   // vector-memory instructions per k-step
+  static constexpr int kDsw = 0;     // LDS write instructions per k-step
   __amdgpu_buffer_rsrc_t rs;
-  uint32_t off0;    // per-thread byte offset at k-step 0
-  uint32_t ldb;     // leading dimension in bytes
-  int r0, c0;
+  uint32_t voff[NQ];
+  int w;
 
   // base: address of (row 0 of the tile, k = 0); rows_left: valid rows from base
   __device__ __forceinline__ void init(const uint16_t* base, int64_t rows_left, int64_t ld) {
-    const int tid = threadIdx.x;
-    ldb = (uint32_t)(ld * 2);
+    const int lane = threadIdx.x & 63;
+    w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t ldb = (uint32_t)(ld * 2);
     rs = make_rsrc(base, rows_left > 0 ? (uint64_t)rows_left * (uint64_t)ldb : 0);
-    c0 = tid & 7;
-    r0 = tid >> 3;
-    off0 = (uint32_t)r0 * ldb + (uint32_t)c0 * 16u;
-  }
-  __device__ __forceinline__ void load(int kt) {
-    const uint32_t o = off0 + (uint32_t)kt * (kBK * 2);
 #pragma unroll
-    for (int j = 0; j < NV; ++j) v[j] = buf_load16(rs, o + (uint32_t)j * 32u * ldb);
+    for (int j = 0; j < NQ; ++j) {
+      const int q = w * NQ + j;
+      const int r = 8 * q + (lane >> 3);
+      voff[j] = (uint32_t)r * ldb + (uint32_t)((lane & 7) ^ lds_swz(r)) * 16u;
+    }
   }
-  __device__ __forceinline__ void store(uint16_t* s) const {
+  // k-step kt into stage `s` ([R][64] bf16)
+  __device__ __forceinline__ void issue(int kt, uint16_t* s) const {
 #pragma unroll
-    for (int j = 0; j < NV; ++j)
-      *reinterpret_cast<u32x4*>(s + lds_off(r0 + 32 * j, c0)) = v[j];
+    for (int j = 0; j < NQ; ++j) {
+      uint16_t* dst = s + (w * NQ + j) * 8 * kBK;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)dst, 16, voff[j], kt * (kBK * 2), 0, 0);
+    }
   }
+  __device__ __forceinline__ void load(int) {}
+  __device__ __forceinline__ void store(uint16_t*) const {}
 };
 
 // Loader for a tile of R rows x 64 k of a row-contiguous operand (transposed
@@ -68,6 +83,8 @@ struct LoaderKC {
 template <int R>
 struct LoaderRC {
   static constexpr int NB = R / 8;  // 8-row blocks across the tile
+  static constexpr int kVmem = 8;
+  static constexpr int kDsw = 8;
   u32x4 v[8];
   __amdgpu_buffer_rsrc_t rs;
   uint32_t off0;
@@ -86,14 +103,15 @@ struct LoaderRC {
     active = kb < 8;
     off0 = (uint32_t)(kb * 8) * ldb + (uint32_t)(row0 + mb * 8) * 2u;
   }
+  __device__ __forceinline__ void issue(int, uint16_t*) const {}
   __device__ __forceinline__ void load(int kt) {
-    if (!active) return;
+    if (NB * 8 < kThreads && !active) return;
     const uint32_t o = off0 + (uint32_t)kt * (uint32_t)kBK * ldb;
 #pragma unroll
     for (int j = 0; j < 8; ++j) v[j] = buf_load16(rs, o + (uint32_t)j * ldb);
   }
   __device__ __forceinline__ void store(uint16_t* s) const {
-    if (!active) return;
+    if (NB * 8 < kThreads && !active) return;
     // v[kk].d[q] holds elements (2q, 2q+1) of k-row kk.  Output row mm holds
     // k = 0..7 of column mm: dword p = (elem mm of k-row 2p, elem mm of 2p+1).
 #pragma unroll
@@ -107,40 +125,106 @@ struct LoaderRC {
   }
 };
 
-template <bool KC, int R> struct LoaderSel;
-template <int R> struct LoaderSel<true, R> { using type = LoaderKC<R>; };
-template <int R> struct LoaderSel<false, R> { using type = LoaderRC<R>; };
+// The four operand stages of one workgroup.
+struct Stages {
+  uint16_t *a0, *a1, *b0, *b1;
+};
 
-// MFMAs of one 64-deep LDS stage.  As: [BM][64], Bs: [BN][64].
+template <int MI, int NI>
+__device__ __forceinline__ void load_frags(const uint16_t* __restrict__ As, const uint16_t* __restrict__ Bs,
+                                           bf16x8 (&a)[MI], bf16x8 (&b)[NI], int arow0, int brow0, int lane, int s) {
+  const int lr = lane & 31;
+  const int ch = 2 * s + (lane >> 5);
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+    a[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(As + lds_off(arow0 + 32 * i + lr, ch)));
+#pragma unroll
+  for (int j = 0; j < NI; ++j)
+    b[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(Bs + lds_off(brow0 + 32 * j + lr, ch)));
+}
+
+// MFMAs of one 64-deep LDS stage (As: [BM][64], Bs: [BN][64]); the operand
+// fragments of sub-step s+1 are fetched while the MFMAs of sub-step s run.
 template <int MI, int NI>
 __device__ __forceinline__ void mma_stage(const uint16_t* __restrict__ As, const uint16_t* __restrict__ Bs,
                                           f32x16 (&acc)[MI][NI], int arow0, int brow0, int lane) {
-  const int lr = lane & 31;
-  const int hk = lane >> 5;
+  bf16x8 a[2][MI], b[2][NI];
+  load_frags<MI, NI>(As, Bs, a[0], b[0], arow0, brow0, lane, 0);
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
-    bf16x8 a[MI], b[NI];
-#pragma unroll
-    for (int i = 0; i < MI; ++i)
-      a[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(As + lds_off(arow0 + 32 * i + lr, 2 * s + hk)));
-#pragma unroll
-    for (int j = 0; j < NI; ++j)
-      b[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(Bs + lds_off(brow0 + 32 * j + lr, 2 * s + hk)));
+    if (s < 3) load_frags<MI, NI>(As, Bs, a[(s + 1) & 1], b[(s + 1) & 1], arow0, brow0, lane, s + 1);
 #pragma unroll
     for (int i = 0; i < MI; ++i)
 #pragma unroll
       for (int j = 0; j < NI; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s & 1][i], b[s & 1][j], acc[i][j], 0, 0, 0);
   }
 }
 
-// Full K loop for one output tile: acc += A_tile * B_tile^T over nk steps.
-// lds must hold 2 * (BM + BN) * 64 bf16.  Ends with a barrier, so the LDS
-// can be reused (or the next tile started) immediately after.
+// Instruction-order hints for one k-step (a single basic block): the first
+// sub-step's fragment reads, then per sub-step its MFMAs with, one after
+// each MFMA, the next sub-step's fragment reads and this k-step's global
+// loads (front-loaded so they have most of the k-step to land), and finally
+// the LDS writes of register-staged operands.
+template <int NM, int NR, int NV>
+__device__ __forceinline__ void sched_substep() {
+  if constexpr (NM > 0) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if constexpr (NR > 0) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      sched_substep<NM - 1, NR - 1, NV>();
+    } else if constexpr (NV > 0) {
+      __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
+      sched_substep<NM - 1, 0, NV - 1>();
+    } else {
+      sched_substep<NM - 1, 0, 0>();
+    }
+  }
+}
+
+template <int MI, int NI, int NVM, int NDSW>
+__device__ __forceinline__ void sched_kstep() {
+  constexpr int NM = MI * NI, NR = MI + NI;
+  constexpr int room = NM - NR;  // MFMA slots left after the reads
+  constexpr int V0 = NVM < room ? NVM : room;
+  constexpr int V1 = (NVM - V0) < room ? (NVM - V0) : room;
+  constexpr int V2 = (NVM - V0 - V1) < room ? (NVM - V0 - V1) : room;
+  constexpr int V3 = NVM - V0 - V1 - V2;
+  __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
+  sched_substep<NM, NR, V0>();
+  sched_substep<NM, NR, V1>();
+  sched_substep<NM, NR, V2>();
+  sched_substep<NM, 0, V3>();
+  if constexpr (NDSW > 0) __builtin_amdgcn_sched_group_barrier(0x200, NDSW, 0);
+}
+
+__device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// One k-step: start the loads of step kn into (na, nb), run the MFMAs of
+// (ca, cb), finish register-staged stores, wait for this wave's loads and
+// meet the other waves at the barrier.
 template <int MI, int NI, class LA, class LB>
-__device__ __forceinline__ void gemm_tile(LA& la, LB& lb, int nk, uint16_t* lds, f32x16 (&acc)[MI][NI]) {
-  constexpr int BM = 64 * MI, BN = 64 * NI;
-  constexpr int STAGE = (BM + BN) * kBK;
+__device__ __forceinline__ void kstep(LA& la, LB& lb, int kn, const uint16_t* ca, const uint16_t* cb, uint16_t* na,
+                                      uint16_t* nb, f32x16 (&acc)[MI][NI], int arow0, int brow0, int lane) {
+  la.issue(kn, na);
+  lb.issue(kn, nb);
+  la.load(kn);
+  lb.load(kn);
+  mma_stage<MI, NI>(ca, cb, acc, arow0, brow0, lane);
+  la.store(na);
+  lb.store(nb);
+  sched_kstep<MI, NI, LA::kVmem + LB::kVmem, LA::kDsw + LB::kDsw>();
+  wait_vm0();
+  __syncthreads();
+}
+
+// Full K loop for one output tile: acc = A_tile * B_tile^T over nk steps,
+// ping-ponging between the stage pairs (a0, b0) and (a1, b1).  Ends with a
+// barrier, so the stages can be reused immediately after.  The last step
+// re-fetches itself into the idle stage (never read), which keeps every
+// step identical.
+template <int MI, int NI, class LA, class LB>
+__device__ __forceinline__ void gemm_tile(LA& la, LB& lb, int nk, const Stages& st, f32x16 (&acc)[MI][NI]) {
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int arow0 = (w & 1) * 32 * MI;
@@ -150,27 +234,29 @@ __device__ __forceinline__ void gemm_tile(LA& la, LB& lb, int nk, uint16_t* lds,
 #pragma unroll
     for (int j = 0; j < NI; ++j) acc[i][j] = f32x16{};
   if (nk <= 0) return;
+  la.issue(0, st.a0);
+  lb.issue(0, st.b0);
   la.load(0);
   lb.load(0);
-  la.store(lds);
-  lb.store(lds + BM * kBK);
+  la.store(st.a0);
+  lb.store(st.b0);
+  wait_vm0();
   __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    uint16_t* cur = lds + (kt & 1) * STAGE;
-    uint16_t* nxt = lds + ((kt + 1) & 1) * STAGE;
-    const bool more = kt + 1 < nk;
-    if (more) {
-      la.load(kt + 1);
-      lb.load(kt + 1);
-    }
-    mma_stage<MI, NI>(cur, cur + BM * kBK, acc, arow0, brow0, lane);
-    if (more) {
-      la.store(nxt);
-      lb.store(nxt + BM * kBK);
-    }
-    __syncthreads();
+  int kt = 0;
+  for (; kt + 1 < nk; kt += 2) {
+    kstep<MI, NI>(la, lb, kt + 1, st.a0, st.b0, st.a1, st.b1, acc, arow0, brow0, lane);
+    kstep<MI, NI>(la, lb, kt + 2 < nk ? kt + 2 : kt + 1, st.a1, st.b1, st.a0, st.b0, acc, arow0, brow0, lane);
   }
+  if (kt < nk) kstep<MI, NI>(la, lb, kt, st.a0, st.b0, st.a1, st.b1, acc, arow0, brow0, lane);
 }
+
+// Declares the four stages of a (BM x 64) + (BN x 64) workgroup in LDS.
+#define KD_DECLARE_STAGES(name, BM, BN)                                   \
+  __shared__ __attribute__((aligned(16))) uint16_t name##_a0[(BM) * kBK]; \
+  __shared__ __attribute__((aligned(16))) uint16_t name##_a1[(BM) * kBK]; \
+  __shared__ __attribute__((aligned(16))) uint16_t name##_b0[(BN) * kBK]; \
+  __shared__ __attribute__((aligned(16))) uint16_t name##_b1[(BN) * kBK]; \
+  const Stages name{name##_a0, name##_a1, name##_b0, name##_b1}
 
 // Position of accumulator element e of subtile (i, j) for this lane, relative
 // to the wave's block: row (M) = 32 i + 8 (e >> 2) + 4 (lane >> 5) + (e & 3),
@@ -186,8 +272,8 @@ __device__ __forceinline__ int xcd_remap(int L, int padded_total) {
 }
 
 // Grouped raster over an (nt x nu) grid of tiles: consecutive ids cover gt
-// token tiles before moving to the next unit, so workgroups running together
-// share both operand tiles through L2.
+// tiles of the first index before moving to the next unit of the second, so
+// workgroups running together share both operand tiles through L2.
 __device__ __forceinline__ void grouped(int id, int nt, int nu, int gt, int& t, int& u) {
   const int gsz = gt * nu;
   const int g = id / gsz;

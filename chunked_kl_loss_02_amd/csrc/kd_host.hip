@@ -34,10 +34,11 @@ struct Plan {
   int64_t nvt;       // vocabulary tiles of 256
   int per, nranges;  // pass 1: vocabulary tiles per workgroup, ranges
   int gt1, gt2;      // token-tile group sizes of pass 1 / pass 2
+  int gv1, gv2;      // vocabulary group sizes (take precedence when > 0)
   int64_t ldp;       // leading dim of the pass-1 partials
   int64_t grows;     // rows of the gradient buffer
   // workspace offsets (bytes)
-  size_t o_G, o_part, o_lse2, o_p, o_pm, o_s, o_neg, o_row, o_bsum, o_scal_f, o_scal_i, o_status, total;
+  size_t o_G, o_Wt, o_hT, o_part, o_lse2, o_p, o_pm, o_s, o_neg, o_row, o_bsum, o_scal_f, o_scal_i, o_status, total;
 };
 
 kd_status check(const kd_problem* p) {
@@ -78,6 +79,8 @@ Plan make_plan(const kd_problem* p) {
   P.nranges = (int)cdiv(P.nvt, P.per);
   P.gt1 = env_int("KDKL_GROUP_T1", 4);
   P.gt2 = env_int("KDKL_GROUP_T2", 4);
+  P.gv1 = env_int("KDKL_GROUP_V1", 8);
+  P.gv2 = env_int("KDKL_GROUP_V2", 8);
   if (P.gt1 < 1) P.gt1 = 1;
   if (P.gt2 < 1) P.gt2 = 1;
   P.ldp = (int64_t)P.ntt_max * 256;
@@ -86,6 +89,8 @@ Plan make_plan(const kd_problem* p) {
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t r = o; o += (bytes + 255) & ~size_t(255); return r; };
   P.o_G = take((size_t)P.grows * P.chunk_v * 2);
+  P.o_Wt = take((size_t)P.H * P.chunk_v * 2);
+  P.o_hT = take((size_t)P.H * P.grows * 2);
   P.o_part = take((size_t)P.nranges * P.ldp * 8);
   P.o_lse2 = take((size_t)Tp * 4);
   P.o_p = take((size_t)P.T * P.K * 4);
@@ -219,6 +224,8 @@ kd_status kd_topk_kl_fwd_bwd(const kd_problem* p, const uint16_t* h, const uint1
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
   uint16_t* G = reinterpret_cast<uint16_t*>(ws + P.o_G);
+  uint16_t* Wt = reinterpret_cast<uint16_t*>(ws + P.o_Wt);
+  uint16_t* hT = reinterpret_cast<uint16_t*>(ws + P.o_hT);
   float2* part = reinterpret_cast<float2*>(ws + P.o_part);
   float* lse2 = reinterpret_cast<float*>(ws + P.o_lse2);
   float* tp = reinterpret_cast<float*>(ws + P.o_p);
@@ -266,6 +273,7 @@ kd_status kd_topk_kl_fwd_bwd(const kd_problem* p, const uint16_t* h, const uint1
     a.per = P.per;
     a.nranges = P.nranges;
     a.gt = std::min(P.gt1, a.ntt);
+    a.gv = std::min(P.gv1, a.nranges);
     a.total = a.ntt * a.nranges;
     a.ldp = (int)P.ldp;
     a.c = c;
@@ -288,10 +296,20 @@ kd_status kd_topk_kl_fwd_bwd(const kd_problem* p, const uint16_t* h, const uint1
     for (int64_t v0 = 0; v0 < V; v0 += P.chunk_v, ++ci) {
       const int64_t vrows = std::min<int64_t>(P.chunk_v, V - v0);
       const int nvt_c = (int)cdiv(vrows, 256);
+      const int64_t vpad = cdiv(vrows, kd::kBK) * kd::kBK;
+      if (dH) {
+        const dim3 tg((unsigned)cdiv(vpad, 64), (unsigned)cdiv(H, 64));
+        L.run(8, [&] { k_transpose<<<tg, 256, 0, s>>>(W + v0 * H, vrows, H, H, vpad, Wt, P.chunk_v); });
+      }
       int bi = 0;
       for (int64_t t0 = 0; t0 < T; t0 += P.Tb, ++bi) {
         const int64_t rows = std::min<int64_t>(P.Tb, T - t0);
         const int ntt = (int)cdiv(rows, 256);
+        const int64_t tpad = cdiv(rows, kd::kBK) * kd::kBK;
+        if (dW && (ci == 0 || P.Tb < T)) {
+          const dim3 tg((unsigned)cdiv(tpad, 64), (unsigned)cdiv(H, 64));
+          L.run(8, [&] { k_transpose<<<tg, 256, 0, s>>>(h + t0 * H, rows, H, H, tpad, hT, P.grows); });
+        }
         kd::Pass2Args a{};
         a.W = W + v0 * H;
         a.h = h + t0 * H;
@@ -305,6 +323,7 @@ kd_status kd_topk_kl_fwd_bwd(const kd_problem* p, const uint16_t* h, const uint1
         a.ntt = ntt;
         a.nvt = nvt_c;
         a.gt = std::min(P.gt2, ntt);
+        a.gv = std::min(P.gv2, nvt_c);
         a.total = ntt * nvt_c;
         a.ldg = P.chunk_v;
         a.c = c;
@@ -316,8 +335,10 @@ kd_status kd_topk_kl_fwd_bwd(const kd_problem* p, const uint16_t* h, const uint1
               v0, vrows, c, G, P.chunk_v);
         });
         kd::BwdArgs b{};
-        b.W = W + v0 * H;
-        b.h = h + t0 * H;
+        b.Wt = Wt;
+        b.hT = hT;
+        b.ldw = P.chunk_v;
+        b.ldt = (int)P.grows;
         b.G = G;
         b.dH = dH ? dH + t0 * H : nullptr;
         b.dW = dW ? dW + v0 * H : nullptr;

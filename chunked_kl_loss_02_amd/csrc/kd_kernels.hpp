@@ -162,17 +162,20 @@ struct Pass1Args {
   const uint16_t* h;     // token block origin [rows, H]
   float2* part;          // [nranges, ldp]
   int64_t V, H, rows;    // rows = valid tokens in the block
-  int ntt, nvt, per, nranges, gt, total, ldp;
+  int ntt, nvt, per, nranges, gt, gv, total, ldp;  // gv > 0: group vocabulary ranges instead
   float c;               // log2(e) / tau
 };
 
-__global__ void __launch_bounds__(256, 1) k_pass1(Pass1Args a) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * 512 * kBK];
+__global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) k_pass1(Pass1Args a) {
+  KD_DECLARE_STAGES(st, 256, 256);
   __shared__ float2 red[2][128];
   const int id = xcd_remap(blockIdx.x, gridDim.x);
   if (id >= a.total) return;
   int tt, vr;
-  grouped(id, a.ntt, a.nranges, a.gt, tt, vr);
+  if (a.gv > 0)
+    grouped(id, a.nranges, a.ntt, a.gv, vr, tt);
+  else
+    grouped(id, a.ntt, a.nranges, a.gt, tt, vr);
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int wm = w & 1, wn = w >> 1;
   const int nk = (int)(a.H / kBK);
@@ -187,7 +190,7 @@ __global__ void __launch_bounds__(256, 1) k_pass1(Pass1Args a) {
   for (int vt = vt0; vt < vt1; ++vt) {
     LoaderKC<256> la;
     la.init(a.W + (int64_t)vt * 256 * a.H, a.V - (int64_t)vt * 256, a.H);
-    gemm_tile<4, 4>(la, lb, nk, lds, acc);
+    gemm_tile<4, 4>(la, lb, nk, st, acc);
     // vocabulary rows of this lane: vt*256 + wm*128 + acc_row(i, e)
     const int64_t vbase = (int64_t)vt * 256 + wm * 128;
     const bool ragged = vbase + 128 > a.V;
@@ -304,23 +307,26 @@ struct Pass2Args {
   const float* scal_f;
   uint16_t* G;            // [ntt*256, ldg]
   int64_t vrows, H, rows; // valid vocabulary rows in chunk / tokens in block
-  int ntt, nvt, gt, total, ldg;
+  int ntt, nvt, gt, gv, total, ldg;  // gv > 0: group vocabulary tiles instead
   float c;
 };
 
-__global__ void __launch_bounds__(256, 1) k_pass2(Pass2Args a) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * 512 * kBK];
+__global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) k_pass2(Pass2Args a) {
+  KD_DECLARE_STAGES(st, 256, 256);
   const int id = xcd_remap(blockIdx.x, gridDim.x);
   if (id >= a.total) return;
   int tt, vt;
-  grouped(id, a.ntt, a.nvt, a.gt, tt, vt);
+  if (a.gv > 0)
+    grouped(id, a.nvt, a.ntt, a.gv, vt, tt);
+  else
+    grouped(id, a.ntt, a.nvt, a.gt, tt, vt);
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int wm = w & 1, wn = w >> 1;
   LoaderKC<256> la, lb;
   la.init(a.W + (int64_t)vt * 256 * a.H, a.vrows - (int64_t)vt * 256, a.H);
   lb.init(a.h + (int64_t)tt * 256 * a.H, a.rows - (int64_t)tt * 256, a.H);
   f32x16 acc[4][4];
-  gemm_tile<4, 4>(la, lb, (int)(a.H / kBK), lds, acc);
+  gemm_tile<4, 4>(la, lb, (int)(a.H / kBK), st, acc);
   const float coef = a.scal_f[0];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -365,23 +371,61 @@ __global__ void k_fixup(const int32_t* __restrict__ idx, const float* __restrict
   G[t * ldg + v] = __builtin_bit_cast(uint16_t, (__bf16)g);
 }
 
+// out[c, r] = in[r, c] for r < rows, c < cols (bf16), and 0 for
+// rows <= r < rows_pad; in has leading dimension ldi, out ldo.  64x64 tiles
+// through LDS, 16-byte loads and stores.  Used to give the gradient
+// contractions k-contiguous copies of W (contracted over the vocabulary) and
+// h (contracted over tokens).
+__global__ void __launch_bounds__(256) k_transpose(const uint16_t* __restrict__ in, int64_t rows, int64_t cols,
+                                                   int64_t ldi, int64_t rows_pad, uint16_t* __restrict__ out,
+                                                   int64_t ldo) {
+  __shared__ uint16_t tile[64][64 + 8];
+  const int64_t r0 = (int64_t)blockIdx.x * 64, c0 = (int64_t)blockIdx.y * 64;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int e = tid + 256 * i;  // 512 vectors of 8
+    const int r = e >> 3, cv = (e & 7) * 8;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (r0 + r < rows && c0 + cv < cols) v = *reinterpret_cast<const u32x4*>(in + (r0 + r) * ldi + c0 + cv);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      tile[r][cv + 2 * q] = (uint16_t)(v[q] & 0xFFFFu);
+      tile[r][cv + 2 * q + 1] = (uint16_t)(v[q] >> 16);
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int e = tid + 256 * i;
+    const int c = e >> 3, rv = (e & 7) * 8;
+    if (c0 + c >= cols || r0 + rv >= rows_pad) continue;
+    u32x4 v;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) v[q] = (uint32_t)tile[rv + 2 * q][c] | ((uint32_t)tile[rv + 2 * q + 1][c] << 16);
+    *reinterpret_cast<u32x4*>(out + (c0 + c) * ldo + r0 + rv) = v;
+  }
+}
+
 // dH (over the chunk's vocabulary) and dW (over the block's tokens) from G.
 // Work ids [0, ndh) are dH tiles (hidden tile x token tile, K = vocabulary);
 // the rest are dW tiles (hidden tile x vocabulary tile, K = tokens).  Both
-// are computed transposed so that a lane stores 4 consecutive hidden units.
+// are computed transposed so that a lane stores 4 consecutive hidden units:
+//   dH^T[m, t] = sum_v Wt[m, v] G[t, v]      (Wt = W_chunk^T, k-contiguous)
+//   dW^T[m, v] = sum_t hT[m, t] G[t, v]      (hT = h_block^T, k-contiguous)
 struct BwdArgs {
-  const uint16_t* W;      // chunk origin
-  const uint16_t* h;      // block origin
+  const uint16_t* Wt;     // [H, ldw]: W chunk transposed, zero past vrows
+  const uint16_t* hT;     // [H, ldt]: h block transposed, zero past rows
   const uint16_t* G;      // [*, ldg]
   float* dH;              // block origin [rows, H] (nullable)
   float* dW;              // chunk origin [vrows, H] (nullable)
   int64_t vrows, H, rows; // valid rows
-  int nht, ntt, nvt, ndh, ndw, ldg, grows;  // grows = allocated rows of G
+  int nht, ntt, nvt, ndh, ndw, ldg, grows, ldw, ldt;  // grows = allocated rows of G
   int acc_dh, acc_dw;     // accumulate (1) or overwrite (0)
 };
 
-__global__ void __launch_bounds__(256, 1) k_bwd(BwdArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * 512 * kBK];
+__global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) k_bwd(BwdArgs a) {
+  KD_DECLARE_STAGES(st, 256, 256);
   const int id = blockIdx.x;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int wm = w & 1, wn = w >> 1;
@@ -392,12 +436,10 @@ __global__ void __launch_bounds__(256, 1) k_bwd(BwdArgs a) {
   if (id < a.ndh) {
     mt = id % a.nht;
     nt = id / a.nht;
-    // A(m = hidden, k = vocab) = W[v, m]: row-contiguous; B(k = vocab, n = token) = G[n, v]: k-contiguous
-    LoaderRC<256> la;
-    LoaderKC<256> lb;
-    la.init(a.W, a.vrows, a.H, mt * 256);
+    LoaderKC<256> la, lb;
+    la.init(a.Wt + (int64_t)mt * 256 * a.ldw, a.H - (int64_t)mt * 256, a.ldw);
     lb.init(a.G + (int64_t)nt * 256 * a.ldg, (int64_t)a.grows - (int64_t)nt * 256, a.ldg);
-    gemm_tile<4, 4>(la, lb, (int)((a.vrows + kBK - 1) / kBK), lds, acc);
+    gemm_tile<4, 4>(la, lb, (int)((a.vrows + kBK - 1) / kBK), st, acc);
     out = a.dH;
     nvalid = a.rows;
     acc_mode = a.acc_dh;
@@ -405,12 +447,12 @@ __global__ void __launch_bounds__(256, 1) k_bwd(BwdArgs a) {
     const int j = id - a.ndh;
     mt = j % a.nht;
     nt = j / a.nht;
-    // A(m = hidden, k = token) = h[t, m]; B(k = token, n = vocab) = G[t, n]: both row-contiguous
-    LoaderRC<256> la;
+    // B(k = token, n = vocab) = G[t, n]: row-contiguous
+    LoaderKC<256> la;
     LoaderRC<256> lb;
-    la.init(a.h, a.rows, a.H, mt * 256);
+    la.init(a.hT + (int64_t)mt * 256 * a.ldt, a.H - (int64_t)mt * 256, a.ldt);
     lb.init(a.G, a.grows, a.ldg, nt * 256);
-    gemm_tile<4, 4>(la, lb, (int)((a.rows + kBK - 1) / kBK), lds, acc);
+    gemm_tile<4, 4>(la, lb, (int)((a.rows + kBK - 1) / kBK), st, acc);
     out = a.dW;
     nvalid = a.vrows;
     acc_mode = a.acc_dw;
