@@ -66,17 +66,12 @@ def cpu_baseline(x, tau, rows: int, seed: int = 0):
     lg = x["teacher_logit"].index_select(0, st).cpu().numpy()
     m = x["mask"].index_select(0, st).cpu().numpy()
     cores = len(os.sched_getaffinity(0))
-    try:
-        from threadpoolctl import threadpool_limits, threadpool_info
-        ctx = threadpool_limits(limits=cores)
+    from threadpoolctl import threadpool_limits, threadpool_info
+    with threadpool_limits(limits=cores):
         used = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:  # pragma: no cover
-        ctx, used = None, cores
-    t0 = time.perf_counter()
-    kl_dense(h, W, idx, lg, m, tau)
-    dt = time.perf_counter() - t0
-    if ctx is not None:
-        ctx.unregister() if hasattr(ctx, "unregister") else None
+        t0 = time.perf_counter()
+        kl_dense(h, W, idx, lg, m, tau)
+        dt = time.perf_counter() - t0
     return {"value": len(sel) / dt, "unit": "tokens/s", "cores": int(used), "kind": "oracle",
             "sample": f"{len(sel)} of {T} tokens (seeded), full V={x['W'].shape[0]}, loss + dH rows + dW in fp64",
             "seconds": dt}
@@ -107,13 +102,16 @@ def run_one(args, wl):
     torch.cuda.synchronize()
     ws_bytes = kd.workspace_size(T, H, V, K, tau)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    outs = (torch.empty((), dtype=torch.float32, device=dev),
+            torch.empty((T, H), dtype=torch.float32, device=dev),
+            torch.empty((V, H), dtype=torch.float32, device=dev))
 
     def step():
-        return kd.fwd_bwd(x["h"], x["W"], x["teacher_idx"], x["teacher_logit"], x["mask"], tau, workspace=ws)
+        return kd.fwd_bwd(x["h"], x["W"], x["teacher_idx"], x["teacher_logit"], x["mask"], tau,
+                          workspace=ws, out=outs)
 
     for _ in range(args.warmup):
-        out = step()
-        del out
+        step()
     torch.cuda.synchronize()
     base_alloc = torch.cuda.memory_allocated(dev)
     torch.cuda.reset_peak_memory_stats(dev)
@@ -121,14 +119,13 @@ def run_one(args, wl):
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        out = step()
+        step()
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
     kd.timing_enable(False)
     per_kernel = kd.timing_collect()
     peak = torch.cuda.max_memory_allocated(dev)
-    loss = out[0].item()
-    del out
+    loss = outs[0].item()
     ms_step = dt * 1e3 / args.steps
     bwd_ms, bwd_n = per_kernel["bwd"]
     bwd_flops_total = 4.0 * T * H * V * args.steps       # dH + dW contractions
@@ -157,7 +154,7 @@ def run_one(args, wl):
         "mfma_util_total": flops_per_token(H, V) * T * args.steps / dt / 1e12 / PEAK_BF16_TFLOPS,
         "per_kernel_ms_per_step": {k: v[0] / args.steps for k, v in per_kernel.items() if v[1]},
         "peak_mem_bytes": int(peak),
-        "peak_mem_above_inputs_bytes": int(peak - base_alloc),
+        "peak_mem_inputs_outputs_workspace_bytes": int(base_alloc),
         "workspace_bytes": int(ws_bytes),
         "naive_logits_bytes": naive_logit_bytes(T, V),
         "loss": loss,
@@ -186,7 +183,7 @@ def main():
     ap.add_argument("--seed", type=int, default=1)
     ap.add_argument("--workload", default="gptoss", choices=["gptoss", "long", "qwen", "tiny"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=512)
+    ap.add_argument("--cpu-rows", type=int, default=2048)
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--sweep", action="store_true")
     args = ap.parse_args()

@@ -90,13 +90,14 @@ def _ptr(t):
 
 def fwd_bwd(h, W, teacher_idx, teacher_logit, mask=None, tau=1.0, *, chunk_v=0, block_t=0,
             grad_h=True, grad_w=True, row_loss=False, validate=False, workspace=None,
-            return_workspace=False):
+            return_workspace=False, out=None):
     """loss, dH, dW [, row_loss] [, workspace] of the fused chunked top-K KL loss.
 
     h [T,H] bf16, W [V,H] bf16, teacher_idx [T,K] int32, teacher_logit [T,K]
     fp32, mask [T] uint8/bool or None; all contiguous on the same GPU.  dH and
     dW are fp32 (None when not requested); loss is a 0-d fp32 tensor.  Runs on
-    torch's current stream; returns without synchronising."""
+    torch's current stream; returns without synchronising.  `out` may pass
+    preallocated (loss, dH, dW[, row_loss]) tensors to be overwritten."""
     import torch
     T, H = h.shape
     V = W.shape[0]
@@ -123,22 +124,31 @@ def fwd_bwd(h, W, teacher_idx, teacher_logit, mask=None, tau=1.0, *, chunk_v=0, 
     _raise(lib().kd_topk_kl_workspace_size(ctypes.byref(prob), ctypes.byref(n)))
     if workspace is None or workspace.numel() < n.value:
         workspace = torch.empty(max(n.value, 256), dtype=torch.uint8, device=dev)
-    loss = torch.empty((), dtype=torch.float32, device=dev)
-    dH = torch.empty((T, H), dtype=torch.float32, device=dev) if grad_h else None
-    dW = torch.empty((V, H), dtype=torch.float32, device=dev) if grad_w else None
-    rl = torch.empty((T,), dtype=torch.float32, device=dev) if row_loss else None
+    if out is not None:
+        loss, dH, dW = out[0], out[1], out[2]
+        rl = out[3] if row_loss else None
+        for t, shp in ((loss, ()), (dH, (T, H)), (dW, (V, H)), (rl, (T,))):
+            if t is not None and (t.dtype != torch.float32 or tuple(t.shape) != shp or not t.is_contiguous()
+                                  or t.device != dev):
+                raise ValueError("preallocated outputs must be contiguous fp32 of the right shapes")
+        grad_h, grad_w = dH is not None, dW is not None
+    else:
+        loss = torch.empty((), dtype=torch.float32, device=dev)
+        dH = torch.empty((T, H), dtype=torch.float32, device=dev) if grad_h else None
+        dW = torch.empty((V, H), dtype=torch.float32, device=dev) if grad_w else None
+        rl = torch.empty((T,), dtype=torch.float32, device=dev) if row_loss else None
     stream = torch.cuda.current_stream(dev).cuda_stream
     code = lib().kd_topk_kl_fwd_bwd(ctypes.byref(prob), _ptr(h), _ptr(W), _ptr(teacher_idx),
                                     _ptr(teacher_logit), _ptr(mask), _ptr(loss), _ptr(dH), _ptr(dW),
                                     _ptr(rl), _ptr(workspace), ctypes.c_size_t(workspace.numel()),
                                     ctypes.c_void_p(stream))
     _raise(code)
-    out = [loss, dH, dW]
+    res = [loss, dH, dW]
     if row_loss:
-        out.append(rl)
+        res.append(rl)
     if return_workspace:
-        out.append(workspace)
-    return tuple(out)
+        res.append(workspace)
+    return tuple(res)
 
 
 def lse(workspace, T, H, V, K, tau=1.0, chunk_v=0, block_t=0):

@@ -1,0 +1,23 @@
+"""Numbers the pages print, checked against the formulas this build reports."""
+import json
+import os
+
+import bench
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def test_dense_teacher_tensor_size_matches_the_blog():
+    g = json.load(open(os.path.join(HERE, "golden", "blog_dense_teacher_tensor.json")))
+    B, V, T = g["shape"]
+    n = bench.naive_logit_bytes(B * T, V, g["bytes_per_element"])
+    assert n == 4 * 201088 * 32768 * 2
+    # "about 50 GB": 52.7e9 bytes = 49.1 GiB
+    assert abs(n / 1e9 - g["stated_gigabytes_approx"]) / g["stated_gigabytes_approx"] < 0.06
+    assert abs(n / 2**30 - g["stated_gigabytes_approx"]) / g["stated_gigabytes_approx"] < 0.06
+
+
+def test_flops_per_token():
+    # pass-1 GEMM, pass-2 recompute, dH and dW: 2*H*V each
+    assert bench.flops_per_token(2880, 201088) == 8 * 2880 * 201088
+    assert abs(bench.flops_per_token(2880, 201088) / 1e9 - 4.633) < 1e-3
