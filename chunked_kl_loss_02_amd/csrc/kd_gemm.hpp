@@ -3,8 +3,11 @@
 // One workgroup = 256 threads = 4 wave64s arranged 2 (M) x 2 (N).  A wave
 // owns a (32*MI) x (32*NI) block of the output tile, held in MI*NI
 // v_mfma_f32_32x32x16_bf16 accumulators (16 fp32 per lane each).  K advances
-// 64 at a time through two LDS stages per operand; the loads of step k+1 are
-// in flight while the MFMAs of step k run, so one barrier per step suffices.
+// 64 at a time (four MFMA sub-steps of 16) through two LDS stages per
+// operand; the loads of step k+1 are in flight while the MFMAs of step k run,
+// so one barrier per step suffices.  That barrier sits between sub-steps 2
+// and 3: sub-step 3's fragments are already in registers, so its MFMAs cover
+// the fetch of the next stage's first fragments after the barrier.
 //
 // Operands are loaded with raw buffer loads whose range ends exactly at the
 // last valid row: out-of-range rows read as zero, which covers the ragged
@@ -143,29 +146,18 @@ __device__ __forceinline__ void load_frags(const uint16_t* __restrict__ As, cons
     b[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(Bs + lds_off(brow0 + 32 * j + lr, ch)));
 }
 
-// MFMAs of one 64-deep LDS stage (As: [BM][64], Bs: [BN][64]); the operand
-// fragments of sub-step s+1 are fetched while the MFMAs of sub-step s run.
 template <int MI, int NI>
-__device__ __forceinline__ void mma_stage(const uint16_t* __restrict__ As, const uint16_t* __restrict__ Bs,
-                                          f32x16 (&acc)[MI][NI], int arow0, int brow0, int lane) {
-  bf16x8 a[2][MI], b[2][NI];
-  load_frags<MI, NI>(As, Bs, a[0], b[0], arow0, brow0, lane, 0);
+__device__ __forceinline__ void mfma_substep(f32x16 (&acc)[MI][NI], const bf16x8 (&a)[MI], const bf16x8 (&b)[NI]) {
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    if (s < 3) load_frags<MI, NI>(As, Bs, a[(s + 1) & 1], b[(s + 1) & 1], arow0, brow0, lane, s + 1);
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
-    for (int i = 0; i < MI; ++i)
-#pragma unroll
-      for (int j = 0; j < NI; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s & 1][i], b[s & 1][j], acc[i][j], 0, 0, 0);
-  }
+    for (int j = 0; j < NI; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
 }
 
-// Instruction-order hints for one k-step (a single basic block): the first
-// sub-step's fragment reads, then per sub-step its MFMAs with, one after
-// each MFMA, the next sub-step's fragment reads and this k-step's global
-// loads (front-loaded so they have most of the k-step to land), and finally
-// the LDS writes of register-staged operands.
+// Instruction-order hints for one scheduling region: per sub-step, its MFMAs
+// with, one after each MFMA, the next sub-step's fragment reads and then this
+// k-step's global loads.
 template <int NM, int NR, int NV>
 __device__ __forceinline__ void sched_substep() {
   if constexpr (NM > 0) {
@@ -182,47 +174,57 @@ __device__ __forceinline__ void sched_substep() {
   }
 }
 
-template <int MI, int NI, int NVM, int NDSW>
-__device__ __forceinline__ void sched_kstep() {
-  constexpr int NM = MI * NI, NR = MI + NI;
-  constexpr int room = NM - NR;  // MFMA slots left after the reads
-  constexpr int V0 = NVM < room ? NVM : room;
-  constexpr int V1 = (NVM - V0) < room ? (NVM - V0) : room;
-  constexpr int V2 = (NVM - V0 - V1) < room ? (NVM - V0 - V1) : room;
-  constexpr int V3 = NVM - V0 - V1 - V2;
-  __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
-  sched_substep<NM, NR, V0>();
-  sched_substep<NM, NR, V1>();
-  sched_substep<NM, NR, V2>();
-  sched_substep<NM, 0, V3>();
-  if constexpr (NDSW > 0) __builtin_amdgcn_sched_group_barrier(0x200, NDSW, 0);
-}
-
 __device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void wait_all() { asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory"); }
 
-// One k-step: start the loads of step kn into (na, nb), run the MFMAs of
-// (ca, cb), finish register-staged stores, wait for this wave's loads and
-// meet the other waves at the barrier.
+// One k-step over stage (ca, cb) while step kn streams into (na, nb).
+//   region 1: the loads of step kn, sub-steps 0..2 (their MFMAs interleaved
+//             with the fragment reads of sub-steps 1..3 and the loads),
+//             register-staged LDS writes, then wait for this wave's loads
+//             and LDS traffic and meet the other waves;
+//   region 2: the first fragments of (na, nb) load under sub-step 3's MFMAs,
+//             whose fragments are already in registers, so the barrier's
+//             bubble is short.
+// On entry a[0], b[0] hold sub-step 0 of (ca, cb); on exit of (na, nb).
 template <int MI, int NI, class LA, class LB>
 __device__ __forceinline__ void kstep(LA& la, LB& lb, int kn, const uint16_t* ca, const uint16_t* cb, uint16_t* na,
-                                      uint16_t* nb, f32x16 (&acc)[MI][NI], int arow0, int brow0, int lane) {
+                                      uint16_t* nb, f32x16 (&acc)[MI][NI], bf16x8 (&a)[2][MI], bf16x8 (&b)[2][NI],
+                                      int arow0, int brow0, int lane) {
+  constexpr int NM = MI * NI, NR = MI + NI;
+  constexpr int NVM = LA::kVmem + LB::kVmem, NDSW = LA::kDsw + LB::kDsw;
+  constexpr int room = NM - NR;
+  constexpr int V0 = NVM < room ? NVM : room;
+  constexpr int V1 = (NVM - V0) < room ? (NVM - V0) : room;
+  constexpr int V2 = NVM - V0 - V1;
+  static_assert(V2 <= room, "too many loads for one k-step");
   la.issue(kn, na);
   lb.issue(kn, nb);
   la.load(kn);
   lb.load(kn);
-  mma_stage<MI, NI>(ca, cb, acc, arow0, brow0, lane);
+#pragma unroll
+  for (int s = 0; s < 3; ++s) {
+    load_frags<MI, NI>(ca, cb, a[(s + 1) & 1], b[(s + 1) & 1], arow0, brow0, lane, s + 1);
+    mfma_substep<MI, NI>(acc, a[s & 1], b[s & 1]);
+  }
   la.store(na);
   lb.store(nb);
-  sched_kstep<MI, NI, LA::kVmem + LB::kVmem, LA::kDsw + LB::kDsw>();
-  wait_vm0();
+  sched_substep<NM, NR, V0>();
+  sched_substep<NM, NR, V1>();
+  sched_substep<NM, NR, V2>();
+  if constexpr (NDSW > 0) __builtin_amdgcn_sched_group_barrier(0x200, NDSW, 0);
+  wait_all();
   __syncthreads();
+  load_frags<MI, NI>(na, nb, a[0], b[0], arow0, brow0, lane, 0);
+  mfma_substep<MI, NI>(acc, a[1], b[1]);
+  sched_substep<NM, NR, 0>();
 }
 
 // Full K loop for one output tile: acc = A_tile * B_tile^T over nk steps,
-// ping-ponging between the stage pairs (a0, b0) and (a1, b1).  Ends with a
-// barrier, so the stages can be reused immediately after.  The last step
-// re-fetches itself into the idle stage (never read), which keeps every
-// step identical.
+// ping-ponging between the stage pairs (a0, b0) and (a1, b1).  Ends with
+// every wave past a barrier that follows its last reads of the stages, so
+// the LDS can be reused (or the next tile started) right after.  The last
+// step re-fetches itself into the idle stage (never consumed), which keeps
+// every step identical.
 template <int MI, int NI, class LA, class LB>
 __device__ __forceinline__ void gemm_tile(LA& la, LB& lb, int nk, const Stages& st, f32x16 (&acc)[MI][NI]) {
   const int lane = threadIdx.x & 63;
@@ -234,20 +236,26 @@ __device__ __forceinline__ void gemm_tile(LA& la, LB& lb, int nk, const Stages& 
 #pragma unroll
     for (int j = 0; j < NI; ++j) acc[i][j] = f32x16{};
   if (nk <= 0) return;
+  bf16x8 a[2][MI], b[2][NI];
   la.issue(0, st.a0);
   lb.issue(0, st.b0);
   la.load(0);
   lb.load(0);
   la.store(st.a0);
   lb.store(st.b0);
-  wait_vm0();
+  wait_all();
   __syncthreads();
+  load_frags<MI, NI>(st.a0, st.b0, a[0], b[0], arow0, brow0, lane, 0);
   int kt = 0;
   for (; kt + 1 < nk; kt += 2) {
-    kstep<MI, NI>(la, lb, kt + 1, st.a0, st.b0, st.a1, st.b1, acc, arow0, brow0, lane);
-    kstep<MI, NI>(la, lb, kt + 2 < nk ? kt + 2 : kt + 1, st.a1, st.b1, st.a0, st.b0, acc, arow0, brow0, lane);
+    kstep<MI, NI>(la, lb, kt + 1, st.a0, st.b0, st.a1, st.b1, acc, a, b, arow0, brow0, lane);
+    kstep<MI, NI>(la, lb, kt + 2 < nk ? kt + 2 : kt + 1, st.a1, st.b1, st.a0, st.b0, acc, a, b, arow0, brow0, lane);
   }
-  if (kt < nk) kstep<MI, NI>(la, lb, kt, st.a0, st.b0, st.a1, st.b1, acc, arow0, brow0, lane);
+  if (kt < nk) kstep<MI, NI>(la, lb, kt, st.a0, st.b0, st.a1, st.b1, acc, a, b, arow0, brow0, lane);
+  // the last region read the idle stage's first fragments: let every wave
+  // finish its LDS reads before anyone reuses the stages
+  wait_all();
+  __syncthreads();
 }
 
 // Declares the four stages of a (BM x 64) + (BN x 64) workgroup in LDS.

@@ -35,6 +35,7 @@ struct Plan {
   int per, nranges;  // pass 1: vocabulary tiles per workgroup, ranges
   int gt1, gt2;      // token-tile group sizes of pass 1 / pass 2
   int gv1, gv2;      // vocabulary group sizes (take precedence when > 0)
+  int gm_dh, gm_dw;  // hidden-tile group sizes of the gradient contractions
   int64_t ldp;       // leading dim of the pass-1 partials
   int64_t grows;     // rows of the gradient buffer
   // workspace offsets (bytes)
@@ -81,6 +82,8 @@ Plan make_plan(const kd_problem* p) {
   P.gt2 = env_int("KDKL_GROUP_T2", 4);
   P.gv1 = env_int("KDKL_GROUP_V1", 8);
   P.gv2 = env_int("KDKL_GROUP_V2", 8);
+  P.gm_dh = std::max(1, env_int("KDKL_GROUP_MDH", 4));
+  P.gm_dw = std::max(1, env_int("KDKL_GROUP_MDW", 2));
   if (P.gt1 < 1) P.gt1 = 1;
   if (P.gt2 < 1) P.gt2 = 1;
   P.ldp = (int64_t)P.ntt_max * 256;
@@ -350,11 +353,15 @@ kd_status kd_topk_kl_fwd_bwd(const kd_problem* p, const uint16_t* h, const uint1
         b.nvt = nvt_c;
         b.ndh = dH ? nht * ntt : 0;
         b.ndw = dW ? nht * nvt_c : 0;
+        b.ndh_pad = (int)(cdiv(b.ndh, 8) * 8);
+        b.ndw_pad = (int)(cdiv(b.ndw, 8) * 8);
+        b.gm_dh = std::min(P.gm_dh, nht);
+        b.gm_dw = std::min(P.gm_dw, nht);
         b.ldg = P.chunk_v;
         b.grows = (int)P.grows;
         b.acc_dh = ci > 0;
         b.acc_dw = bi > 0;
-        L.run(7, [&] { k_bwd<<<b.ndh + b.ndw, 256, 0, s>>>(b); });
+        L.run(7, [&] { k_bwd<<<b.ndh_pad + b.ndw_pad, 256, 0, s>>>(b); });
       }
     }
   }

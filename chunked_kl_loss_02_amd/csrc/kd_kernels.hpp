@@ -327,30 +327,48 @@ __global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 
   lb.init(a.h + (int64_t)tt * 256 * a.H, a.rows - (int64_t)tt * 256, a.H);
   f32x16 acc[4][4];
   gemm_tile<4, 4>(la, lb, (int)(a.H / kBK), st, acc);
+  // The bf16 tile goes through LDS (the four stages, 4 x 32 KiB, are free
+  // after gemm_tile; 64 token rows each) as [256 tokens][256 vocab] rows of
+  // 32 16-byte chunks, chunk c of row t at position c ^ (t & 31), then leaves
+  // as full 512-byte row segments of G.
+  auto row = [&](int tl) -> uint16_t* {
+    uint16_t* b = tl < 64 ? st.a0 : tl < 128 ? st.a1 : tl < 192 ? st.b0 : st.b1;
+    return b + (tl & 63) * 256;
+  };
   const float coef = a.scal_f[0];
+  const int vl0 = vt * 256 + wm * 128;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int t = tt * 256 + wn * 128 + acc_col(j, lane);
+    const int tl = wn * 128 + acc_col(j, lane);  // token row inside the tile
+    const int t = tt * 256 + tl;
     const bool tv = t < a.rows && (a.mask ? a.mask[t] != 0 : true);
     const float l2 = tv ? a.lse2[t] : 0.f;
     const float cf = tv ? coef : 0.f;
-    uint16_t* grow = a.G + (int64_t)t * a.ldg;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int vl = vt * 256 + wm * 128 + acc_row(i, 4 * q, lane);  // 4 consecutive rows
+        const int vr = wm * 128 + acc_row(i, 4 * q, lane);  // 4 consecutive vocabulary rows
         float g[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const float x = cf * fast_exp2(fmaf(acc[i][j][4 * q + r], a.c, -l2));
-          g[r] = (vl + r < a.vrows) ? x : 0.f;
+          g[r] = (vl0 - wm * 128 + vr + r < a.vrows) ? x : 0.f;
         }
         u32x2 pk;
         pk[0] = pack_bf16x2(g[0], g[1]);
         pk[1] = pack_bf16x2(g[2], g[3]);
-        *reinterpret_cast<u32x2*>(grow + vl) = pk;
+        const int pos = ((vr >> 3) ^ (tl & 31)) * 8 + (vr & 7);
+        *reinterpret_cast<u32x2*>(row(tl) + pos) = pk;
       }
+  }
+  __syncthreads();
+  const int tid = threadIdx.x;
+#pragma unroll 4
+  for (int e = tid; e < 256 * 32; e += 256) {
+    const int tl = e >> 5, c = e & 31;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(row(tl) + ((c ^ (tl & 31)) * 8));
+    *reinterpret_cast<u32x4*>(a.G + (int64_t)(tt * 256 + tl) * a.ldg + vt * 256 + c * 8) = v;
   }
 }
 
@@ -421,21 +439,28 @@ struct BwdArgs {
   float* dW;              // chunk origin [vrows, H] (nullable)
   int64_t vrows, H, rows; // valid rows
   int nht, ntt, nvt, ndh, ndw, ldg, grows, ldw, ldt;  // grows = allocated rows of G
+  int ndh_pad, ndw_pad;   // segment sizes rounded up to multiples of 8
+  int gm_dh, gm_dw;       // hidden-tile group sizes of the two rasters
   int acc_dh, acc_dw;     // accumulate (1) or overwrite (0)
 };
 
+// Grid: [0, ndh_pad) dH work, then [ndh_pad, ndh_pad + ndw_pad) dW work;
+// inside each segment the 8 XCDs get contiguous work ranges (idle padding
+// workgroups exit at once).  dH tiles come first: their K loop (the chunk's
+// vocabulary) is the longer one.
 __global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) k_bwd(BwdArgs a) {
   KD_DECLARE_STAGES(st, 256, 256);
-  const int id = blockIdx.x;
+  const int L = blockIdx.x;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int wm = w & 1, wn = w >> 1;
   f32x16 acc[4][4];
   float* out;
   int64_t nvalid;
   int mt, nt, acc_mode;
-  if (id < a.ndh) {
-    mt = id % a.nht;
-    nt = id / a.nht;
+  if (L < a.ndh_pad) {
+    const int id = xcd_remap(L, a.ndh_pad);
+    if (id >= a.ndh) return;
+    grouped(id, a.nht, a.ntt, a.gm_dh, mt, nt);
     LoaderKC<256> la, lb;
     la.init(a.Wt + (int64_t)mt * 256 * a.ldw, a.H - (int64_t)mt * 256, a.ldw);
     lb.init(a.G + (int64_t)nt * 256 * a.ldg, (int64_t)a.grows - (int64_t)nt * 256, a.ldg);
@@ -444,9 +469,9 @@ __global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 
     nvalid = a.rows;
     acc_mode = a.acc_dh;
   } else {
-    const int j = id - a.ndh;
-    mt = j % a.nht;
-    nt = j / a.nht;
+    const int id = xcd_remap(L - a.ndh_pad, a.ndw_pad);
+    if (id >= a.ndw) return;
+    grouped(id, a.nht, a.nvt, a.gm_dw, mt, nt);
     // B(k = token, n = vocab) = G[t, n]: row-contiguous
     LoaderKC<256> la;
     LoaderRC<256> lb;
