@@ -52,6 +52,7 @@ struct LoaderKC {
   static constexpr int NQ = R / 32;  // wave instructions per wave per k-step
   static constexpr int kVmem = NQ;   // vector-memory instructions per k-step
   static constexpr int kDsw = 0;     // LDS write instructions per k-step
+  static constexpr int kReads = 1;   // LDS read instructions per MFMA fragment
   __amdgpu_buffer_rsrc_t rs;
   uint32_t voff[NQ];
   int w;
@@ -79,6 +80,78 @@ struct LoaderKC {
   }
   __device__ __forceinline__ void load(int) {}
   __device__ __forceinline__ void store(uint16_t*) const {}
+  // MFMA fragment of sub-step s: row rbase + lane % 32, k = 16 s + 8 (lane / 32) + 0..7
+  static __device__ __forceinline__ bf16x8 frag(const uint16_t* st, int rbase, int s, int lane) {
+    return __builtin_bit_cast(bf16x8,
+                              *reinterpret_cast<const u32x4*>(st + lds_off(rbase + (lane & 31), 2 * s + (lane >> 5))));
+  }
+};
+
+// Loader for a tile of 256 rows x 64 k of a row-contiguous operand (element
+// (row, k) at base + k*ld + row: W or h or G contracted over their leading
+// index), global -> LDS without registers and without a transpose: the stage
+// holds the 64 k-rows as they are in memory ([64][256] bf16, 512 B per row),
+// and the MFMA fragments are read with ds_read_b64_tr_b16, which hands lane
+// i of each 16-lane group 4 consecutive k of column i from the 4 rows its
+// group addresses.  16-byte chunk c of k-row r sits at position
+// c ^ kTrMask[r & 3]; the masks {0, 6, 10, 12} put the 4 rows x 2 (or 4)
+// chunks of one transposed read in distinct bank groups.
+struct LoaderTR {
+  static constexpr int NQ = 8;       // 64 rows x 512 B = 32 KiB = 8 x 1 KiB per wave
+  static constexpr int kVmem = NQ;
+  static constexpr int kDsw = 0;
+  static constexpr int kReads = 2;
+  __amdgpu_buffer_rsrc_t rs;
+  uint32_t voff[NQ];
+  uint32_t step_bytes;  // 64 k-rows
+  int w;
+
+  static __device__ __forceinline__ int trm(int r) { return (0xCA60 >> (4 * (r & 3))) & 15; }
+
+  // base: address of (row 0, k = 0) of the operand's k-origin; rows are the
+  // contiguous dimension; row0: first row of the tile; k_left: valid k rows.
+  __device__ __forceinline__ void init(const uint16_t* base, int64_t k_left, int64_t ld, int row0) {
+    const int lane = threadIdx.x & 63;
+    w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t ldb = (uint32_t)(ld * 2);
+    step_bytes = (uint32_t)kBK * ldb;
+    rs = make_rsrc(base, k_left > 0 ? (uint64_t)k_left * (uint64_t)ldb : 0);
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) {
+      const int r = 2 * (w * NQ + j) + (lane >> 5);  // k-row of the stage
+      const int c = (lane & 31) ^ trm(r);           // logical chunk landing in this lane's slot
+      voff[j] = (uint32_t)r * ldb + (uint32_t)row0 * 2u + (uint32_t)c * 16u;
+    }
+  }
+  // the k-step offset goes into the per-lane offset: rows past k_left must
+  // fail the range check, which covers the per-lane offset only
+  __device__ __forceinline__ void issue(int kt, uint16_t* st) const {
+    const uint32_t o = (uint32_t)kt * step_bytes;
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) {
+      uint16_t* dst = st + (w * NQ + j) * 512;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)dst, 16, voff[j] + o, 0, 0, 0);
+    }
+  }
+  __device__ __forceinline__ void load(int) {}
+  __device__ __forceinline__ void store(uint16_t*) const {}
+  static __device__ __forceinline__ bf16x8 frag(const uint16_t* st, int rbase, int s, int lane) {
+    typedef short v4i16 __attribute__((ext_vector_type(4)));
+    const int g = lane >> 4, i = lane & 15;
+    const int col = rbase + 16 * (g & 1) + 4 * (i & 3);  // first of the 4 columns this lane addresses
+    const int kb = 16 * s + 8 * (g >> 1) + (i >> 2);
+    v4i16 v[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int r = kb + 4 * h;
+      const int pos = (((col >> 3) ^ trm(r)) << 3) + (col & 7);
+      v[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) v4i16*)(st + r * 256 + pos));
+    }
+    const short __attribute__((ext_vector_type(8))) x = {v[0][0], v[0][1], v[0][2], v[0][3],
+                                                         v[1][0], v[1][1], v[1][2], v[1][3]};
+    return __builtin_bit_cast(bf16x8, x);
+  }
 };
 
 // Loader for a tile of R rows x 64 k of a row-contiguous operand (transposed
@@ -88,6 +161,7 @@ struct LoaderRC {
   static constexpr int NB = R / 8;  // 8-row blocks across the tile
   static constexpr int kVmem = 8;
   static constexpr int kDsw = 8;
+  static constexpr int kReads = 1;
   u32x4 v[8];
   __amdgpu_buffer_rsrc_t rs;
   uint32_t off0;
@@ -126,6 +200,9 @@ struct LoaderRC {
       *reinterpret_cast<u32x4*>(s + lds_off(mb * 8 + mm, kb)) = y;
     }
   }
+  static __device__ __forceinline__ bf16x8 frag(const uint16_t* st, int rbase, int s, int lane) {
+    return LoaderKC<R>::frag(st, rbase, s, lane);
+  }
 };
 
 // The four operand stages of one workgroup.
@@ -133,17 +210,13 @@ struct Stages {
   uint16_t *a0, *a1, *b0, *b1;
 };
 
-template <int MI, int NI>
+template <int MI, int NI, class LA, class LB>
 __device__ __forceinline__ void load_frags(const uint16_t* __restrict__ As, const uint16_t* __restrict__ Bs,
                                            bf16x8 (&a)[MI], bf16x8 (&b)[NI], int arow0, int brow0, int lane, int s) {
-  const int lr = lane & 31;
-  const int ch = 2 * s + (lane >> 5);
 #pragma unroll
-  for (int i = 0; i < MI; ++i)
-    a[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(As + lds_off(arow0 + 32 * i + lr, ch)));
+  for (int i = 0; i < MI; ++i) a[i] = LA::frag(As, arow0 + 32 * i, s, lane);
 #pragma unroll
-  for (int j = 0; j < NI; ++j)
-    b[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(Bs + lds_off(brow0 + 32 * j + lr, ch)));
+  for (int j = 0; j < NI; ++j) b[j] = LB::frag(Bs, brow0 + 32 * j, s, lane);
 }
 
 template <int MI, int NI>
@@ -162,15 +235,10 @@ template <int NM, int NR, int NV>
 __device__ __forceinline__ void sched_substep() {
   if constexpr (NM > 0) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    if constexpr (NR > 0) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      sched_substep<NM - 1, NR - 1, NV>();
-    } else if constexpr (NV > 0) {
-      __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
-      sched_substep<NM - 1, 0, NV - 1>();
-    } else {
-      sched_substep<NM - 1, 0, 0>();
-    }
+    if constexpr (NR > 0) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    if constexpr (NV > 0 && (NR <= 0 || NR < NM)) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
+    constexpr int nv = (NV > 0 && (NR <= 0 || NR < NM)) ? NV - 1 : NV;
+    sched_substep<NM - 1, (NR > 0 ? NR - 1 : 0), nv>();
   }
 }
 
@@ -190,20 +258,20 @@ template <int MI, int NI, class LA, class LB>
 __device__ __forceinline__ void kstep(LA& la, LB& lb, int kn, const uint16_t* ca, const uint16_t* cb, uint16_t* na,
                                       uint16_t* nb, f32x16 (&acc)[MI][NI], bf16x8 (&a)[2][MI], bf16x8 (&b)[2][NI],
                                       int arow0, int brow0, int lane) {
-  constexpr int NM = MI * NI, NR = MI + NI;
+  constexpr int NM = MI * NI, NR = MI * LA::kReads + NI * LB::kReads;
   constexpr int NVM = LA::kVmem + LB::kVmem, NDSW = LA::kDsw + LB::kDsw;
-  constexpr int room = NM - NR;
-  constexpr int V0 = NVM < room ? NVM : room;
-  constexpr int V1 = (NVM - V0) < room ? (NVM - V0) : room;
+  static_assert(NR <= NM, "more fragment reads than MFMAs in a sub-step");
+  constexpr int V0 = NVM < NM ? NVM : NM;
+  constexpr int V1 = (NVM - V0) < NM ? (NVM - V0) : NM;
   constexpr int V2 = NVM - V0 - V1;
-  static_assert(V2 <= room, "too many loads for one k-step");
+  static_assert(V2 <= NM, "too many loads for one k-step");
   la.issue(kn, na);
   lb.issue(kn, nb);
   la.load(kn);
   lb.load(kn);
 #pragma unroll
   for (int s = 0; s < 3; ++s) {
-    load_frags<MI, NI>(ca, cb, a[(s + 1) & 1], b[(s + 1) & 1], arow0, brow0, lane, s + 1);
+    load_frags<MI, NI, LA, LB>(ca, cb, a[(s + 1) & 1], b[(s + 1) & 1], arow0, brow0, lane, s + 1);
     mfma_substep<MI, NI>(acc, a[s & 1], b[s & 1]);
   }
   la.store(na);
@@ -214,7 +282,7 @@ __device__ __forceinline__ void kstep(LA& la, LB& lb, int kn, const uint16_t* ca
   if constexpr (NDSW > 0) __builtin_amdgcn_sched_group_barrier(0x200, NDSW, 0);
   wait_all();
   __syncthreads();
-  load_frags<MI, NI>(na, nb, a[0], b[0], arow0, brow0, lane, 0);
+  load_frags<MI, NI, LA, LB>(na, nb, a[0], b[0], arow0, brow0, lane, 0);
   mfma_substep<MI, NI>(acc, a[1], b[1]);
   sched_substep<NM, NR, 0>();
 }
@@ -245,7 +313,7 @@ __device__ __forceinline__ void gemm_tile(LA& la, LB& lb, int nk, const Stages& 
   lb.store(st.b0);
   wait_all();
   __syncthreads();
-  load_frags<MI, NI>(st.a0, st.b0, a[0], b[0], arow0, brow0, lane, 0);
+  load_frags<MI, NI, LA, LB>(st.a0, st.b0, a[0], b[0], arow0, brow0, lane, 0);
   int kt = 0;
   for (; kt + 1 < nk; kt += 2) {
     kstep<MI, NI>(la, lb, kt + 1, st.a0, st.b0, st.a1, st.b1, acc, a, b, arow0, brow0, lane);

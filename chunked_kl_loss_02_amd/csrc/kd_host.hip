@@ -39,7 +39,7 @@ struct Plan {
   int64_t ldp;       // leading dim of the pass-1 partials
   int64_t grows;     // rows of the gradient buffer
   // workspace offsets (bytes)
-  size_t o_G, o_Wt, o_hT, o_part, o_lse2, o_p, o_pm, o_s, o_neg, o_row, o_bsum, o_scal_f, o_scal_i, o_status, total;
+  size_t o_G, o_part, o_lse2, o_p, o_pm, o_s, o_neg, o_row, o_bsum, o_scal_f, o_scal_i, o_status, total;
 };
 
 kd_status check(const kd_problem* p) {
@@ -92,8 +92,6 @@ Plan make_plan(const kd_problem* p) {
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t r = o; o += (bytes + 255) & ~size_t(255); return r; };
   P.o_G = take((size_t)P.grows * P.chunk_v * 2);
-  P.o_Wt = take((size_t)P.H * P.chunk_v * 2);
-  P.o_hT = take((size_t)P.H * P.grows * 2);
   P.o_part = take((size_t)P.nranges * P.ldp * 8);
   P.o_lse2 = take((size_t)Tp * 4);
   P.o_p = take((size_t)P.T * P.K * 4);
@@ -139,13 +137,13 @@ struct Launcher {
     if (g_timing) {
       a = pool_get();
       b = pool_get();
-      if (a) hipEventRecord(a, s);
+      if (a) (void)hipEventRecord(a, s);
     }
     f();
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) err = e;
     if (g_timing && a && b) {
-      hipEventRecord(b, s);
+      (void)hipEventRecord(b, s);
       g_launches.push_back({cls, a, b});
     }
   }
@@ -227,8 +225,6 @@ kd_status kd_topk_kl_fwd_bwd(const kd_problem* p, const uint16_t* h, const uint1
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
   uint16_t* G = reinterpret_cast<uint16_t*>(ws + P.o_G);
-  uint16_t* Wt = reinterpret_cast<uint16_t*>(ws + P.o_Wt);
-  uint16_t* hT = reinterpret_cast<uint16_t*>(ws + P.o_hT);
   float2* part = reinterpret_cast<float2*>(ws + P.o_part);
   float* lse2 = reinterpret_cast<float*>(ws + P.o_lse2);
   float* tp = reinterpret_cast<float*>(ws + P.o_p);
@@ -283,7 +279,7 @@ kd_status kd_topk_kl_fwd_bwd(const kd_problem* p, const uint16_t* h, const uint1
     const int grid = (int)(cdiv(a.total, 8) * 8);
     L.run(2, [&] { k_pass1<<<grid, 256, 0, s>>>(a); });
     L.run(3, [&] {
-      k_lse<<<(unsigned)cdiv(rows, 256), 256, 0, s>>>(part, P.nranges, (int)P.ldp, rows, lse2 + t0);
+      k_lse<<<(unsigned)cdiv(rows, 32), 256, 0, s>>>(part, P.nranges, (int)P.ldp, rows, lse2 + t0);
     });
   }
   const int64_t nb = cdiv(T, 256);
@@ -299,20 +295,10 @@ kd_status kd_topk_kl_fwd_bwd(const kd_problem* p, const uint16_t* h, const uint1
     for (int64_t v0 = 0; v0 < V; v0 += P.chunk_v, ++ci) {
       const int64_t vrows = std::min<int64_t>(P.chunk_v, V - v0);
       const int nvt_c = (int)cdiv(vrows, 256);
-      const int64_t vpad = cdiv(vrows, kd::kBK) * kd::kBK;
-      if (dH) {
-        const dim3 tg((unsigned)cdiv(vpad, 64), (unsigned)cdiv(H, 64));
-        L.run(8, [&] { k_transpose<<<tg, 256, 0, s>>>(W + v0 * H, vrows, H, H, vpad, Wt, P.chunk_v); });
-      }
       int bi = 0;
       for (int64_t t0 = 0; t0 < T; t0 += P.Tb, ++bi) {
         const int64_t rows = std::min<int64_t>(P.Tb, T - t0);
         const int ntt = (int)cdiv(rows, 256);
-        const int64_t tpad = cdiv(rows, kd::kBK) * kd::kBK;
-        if (dW && (ci == 0 || P.Tb < T)) {
-          const dim3 tg((unsigned)cdiv(tpad, 64), (unsigned)cdiv(H, 64));
-          L.run(8, [&] { k_transpose<<<tg, 256, 0, s>>>(h + t0 * H, rows, H, H, tpad, hT, P.grows); });
-        }
         kd::Pass2Args a{};
         a.W = W + v0 * H;
         a.h = h + t0 * H;
@@ -338,10 +324,8 @@ kd_status kd_topk_kl_fwd_bwd(const kd_problem* p, const uint16_t* h, const uint1
               v0, vrows, c, G, P.chunk_v);
         });
         kd::BwdArgs b{};
-        b.Wt = Wt;
-        b.hT = hT;
-        b.ldw = P.chunk_v;
-        b.ldt = (int)P.grows;
+        b.W = W + v0 * H;
+        b.h = h + t0 * H;
         b.G = G;
         b.dH = dH ? dH + t0 * H : nullptr;
         b.dW = dW ? dW + v0 * H : nullptr;

@@ -245,17 +245,28 @@ __global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 
   }
 }
 
-// lse2[t] = log2 sum_v 2^(c S[t,v]) from the per-range partials (fixed order).
-__global__ void k_lse(const float2* __restrict__ part, int nranges, int ldp, int64_t rows,
-                      float* __restrict__ lse2) {
-  const int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-  if (t >= rows) return;
+// lse2[t] = log2 sum_v 2^(c S[t,v]) from the per-range partials.  A block
+// handles 32 tokens; its 8 thread groups each fold every 8th range, then the
+// 8 partial results are folded in a fixed order (deterministic).
+__global__ void __launch_bounds__(256) k_lse(const float2* __restrict__ part, int nranges, int ldp, int64_t rows,
+                                             float* __restrict__ lse2) {
+  __shared__ float2 red[8][32];
+  const int tx = threadIdx.x & 31, g = threadIdx.x >> 5;
+  const int64_t t = (int64_t)blockIdx.x * 32 + tx;
   float m = -INFINITY, l = 0.f;
-  for (int r = 0; r < nranges; ++r) {
-    const float2 p = part[(int64_t)r * ldp + t];
-    lse_merge(m, l, p.x, p.y);
+  if (t < rows) {
+    for (int r = g; r < nranges; r += 8) {
+      const float2 p = part[(int64_t)r * ldp + t];
+      lse_merge(m, l, p.x, p.y);
+    }
   }
-  lse2[t] = m + log2f(l);
+  red[g][tx] = make_float2(m, l);
+  __syncthreads();
+  if (g == 0 && t < rows) {
+#pragma unroll
+    for (int k = 1; k < 8; ++k) lse_merge(m, l, red[k][tx].x, red[k][tx].y);
+    lse2[t] = m + log2f(l);
+  }
 }
 
 // Per-row KL and per-block partial sums (fp64, fixed order).
@@ -325,6 +336,19 @@ __global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 
   LoaderKC<256> la, lb;
   la.init(a.W + (int64_t)vt * 256 * a.H, a.vrows - (int64_t)vt * 256, a.H);
   lb.init(a.h + (int64_t)tt * 256 * a.H, a.rows - (int64_t)tt * 256, a.H);
+  // per-token LSE and gradient coefficient of this lane's 4 token columns,
+  // fetched before the K loop so their latency is hidden
+  float l2v[4], cfv[4];
+  {
+    const float coef = a.scal_f[0];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int t = tt * 256 + wn * 128 + acc_col(j, lane);
+      const bool tv = t < a.rows && (a.mask ? a.mask[t] != 0 : true);
+      l2v[j] = tv ? a.lse2[t] : 0.f;
+      cfv[j] = tv ? coef : 0.f;
+    }
+  }
   f32x16 acc[4][4];
   gemm_tile<4, 4>(la, lb, (int)(a.H / kBK), st, acc);
   // The bf16 tile goes through LDS (the four stages, 4 x 32 KiB, are free
@@ -335,15 +359,12 @@ __global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 
     uint16_t* b = tl < 64 ? st.a0 : tl < 128 ? st.a1 : tl < 192 ? st.b0 : st.b1;
     return b + (tl & 63) * 256;
   };
-  const float coef = a.scal_f[0];
   const int vl0 = vt * 256 + wm * 128;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int tl = wn * 128 + acc_col(j, lane);  // token row inside the tile
-    const int t = tt * 256 + tl;
-    const bool tv = t < a.rows && (a.mask ? a.mask[t] != 0 : true);
-    const float l2 = tv ? a.lse2[t] : 0.f;
-    const float cf = tv ? coef : 0.f;
+    const float l2 = l2v[j];
+    const float cf = cfv[j];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -389,56 +410,20 @@ __global__ void k_fixup(const int32_t* __restrict__ idx, const float* __restrict
   G[t * ldg + v] = __builtin_bit_cast(uint16_t, (__bf16)g);
 }
 
-// out[c, r] = in[r, c] for r < rows, c < cols (bf16), and 0 for
-// rows <= r < rows_pad; in has leading dimension ldi, out ldo.  64x64 tiles
-// through LDS, 16-byte loads and stores.  Used to give the gradient
-// contractions k-contiguous copies of W (contracted over the vocabulary) and
-// h (contracted over tokens).
-__global__ void __launch_bounds__(256) k_transpose(const uint16_t* __restrict__ in, int64_t rows, int64_t cols,
-                                                   int64_t ldi, int64_t rows_pad, uint16_t* __restrict__ out,
-                                                   int64_t ldo) {
-  __shared__ uint16_t tile[64][64 + 8];
-  const int64_t r0 = (int64_t)blockIdx.x * 64, c0 = (int64_t)blockIdx.y * 64;
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int e = tid + 256 * i;  // 512 vectors of 8
-    const int r = e >> 3, cv = (e & 7) * 8;
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (r0 + r < rows && c0 + cv < cols) v = *reinterpret_cast<const u32x4*>(in + (r0 + r) * ldi + c0 + cv);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      tile[r][cv + 2 * q] = (uint16_t)(v[q] & 0xFFFFu);
-      tile[r][cv + 2 * q + 1] = (uint16_t)(v[q] >> 16);
-    }
-  }
-  __syncthreads();
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int e = tid + 256 * i;
-    const int c = e >> 3, rv = (e & 7) * 8;
-    if (c0 + c >= cols || r0 + rv >= rows_pad) continue;
-    u32x4 v;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) v[q] = (uint32_t)tile[rv + 2 * q][c] | ((uint32_t)tile[rv + 2 * q + 1][c] << 16);
-    *reinterpret_cast<u32x4*>(out + (c0 + c) * ldo + r0 + rv) = v;
-  }
-}
-
 // dH (over the chunk's vocabulary) and dW (over the block's tokens) from G.
 // Work ids [0, ndh) are dH tiles (hidden tile x token tile, K = vocabulary);
 // the rest are dW tiles (hidden tile x vocabulary tile, K = tokens).  Both
 // are computed transposed so that a lane stores 4 consecutive hidden units:
-//   dH^T[m, t] = sum_v Wt[m, v] G[t, v]      (Wt = W_chunk^T, k-contiguous)
-//   dW^T[m, v] = sum_t hT[m, t] G[t, v]      (hT = h_block^T, k-contiguous)
+//   dH^T[m, t] = sum_v W[v, m] G[t, v]      (W rows read with transposed LDS reads)
+//   dW^T[m, v] = sum_t h[t, m] G[t, v]      (h and G rows read with transposed LDS reads)
 struct BwdArgs {
-  const uint16_t* Wt;     // [H, ldw]: W chunk transposed, zero past vrows
-  const uint16_t* hT;     // [H, ldt]: h block transposed, zero past rows
+  const uint16_t* W;      // chunk origin [vrows, H]
+  const uint16_t* h;      // block origin [rows, H]
   const uint16_t* G;      // [*, ldg]
   float* dH;              // block origin [rows, H] (nullable)
   float* dW;              // chunk origin [vrows, H] (nullable)
   int64_t vrows, H, rows; // valid rows
-  int nht, ntt, nvt, ndh, ndw, ldg, grows, ldw, ldt;  // grows = allocated rows of G
+  int nht, ntt, nvt, ndh, ndw, ldg, grows;  // grows = allocated rows of G
   int ndh_pad, ndw_pad;   // segment sizes rounded up to multiples of 8
   int gm_dh, gm_dw;       // hidden-tile group sizes of the two rasters
   int acc_dh, acc_dw;     // accumulate (1) or overwrite (0)
@@ -461,8 +446,9 @@ __global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 
     const int id = xcd_remap(L, a.ndh_pad);
     if (id >= a.ndh) return;
     grouped(id, a.nht, a.ntt, a.gm_dh, mt, nt);
-    LoaderKC<256> la, lb;
-    la.init(a.Wt + (int64_t)mt * 256 * a.ldw, a.H - (int64_t)mt * 256, a.ldw);
+    LoaderTR la;
+    LoaderKC<256> lb;
+    la.init(a.W, a.vrows, a.H, mt * 256);
     lb.init(a.G + (int64_t)nt * 256 * a.ldg, (int64_t)a.grows - (int64_t)nt * 256, a.ldg);
     gemm_tile<4, 4>(la, lb, (int)((a.vrows + kBK - 1) / kBK), st, acc);
     out = a.dH;
@@ -472,10 +458,8 @@ __global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 
     const int id = xcd_remap(L - a.ndh_pad, a.ndw_pad);
     if (id >= a.ndw) return;
     grouped(id, a.nht, a.nvt, a.gm_dw, mt, nt);
-    // B(k = token, n = vocab) = G[t, n]: row-contiguous
-    LoaderKC<256> la;
-    LoaderRC<256> lb;
-    la.init(a.hT + (int64_t)mt * 256 * a.ldt, a.H - (int64_t)mt * 256, a.ldt);
+    LoaderTR la, lb;
+    la.init(a.h, a.rows, a.H, mt * 256);
     lb.init(a.G, a.grows, a.ldg, nt * 256);
     gemm_tile<4, 4>(la, lb, (int)((a.rows + kBK - 1) / kBK), st, acc);
     out = a.dW;
