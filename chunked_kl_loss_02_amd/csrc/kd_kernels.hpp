@@ -359,12 +359,17 @@ __global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 
     uint16_t* b = tl < 64 ? st.a0 : tl < 128 ? st.a1 : tl < 192 ? st.b0 : st.b1;
     return b + (tl & 63) * 256;
   };
-  const int vl0 = vt * 256 + wm * 128;
+  // G = coef 2^(c S - lse2) = 2^(c S - (lse2 - log2 coef)); a masked or
+  // padding token has coef = 0, i.e. an infinite offset and exact zeros
+  float offv[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) offv[j] = cfv[j] > 0.f ? l2v[j] - log2f(cfv[j]) : INFINITY;
+  const bool full = (int64_t)vt * 256 + 256 <= a.vrows;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int tl = wn * 128 + acc_col(j, lane);  // token row inside the tile
-    const float l2 = l2v[j];
-    const float cf = cfv[j];
+    const float off = offv[j];
+    uint16_t* trow = row(tl);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -372,15 +377,17 @@ __global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 
         const int vr = wm * 128 + acc_row(i, 4 * q, lane);  // 4 consecutive vocabulary rows
         float g[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float x = cf * fast_exp2(fmaf(acc[i][j][4 * q + r], a.c, -l2));
-          g[r] = (vl0 - wm * 128 + vr + r < a.vrows) ? x : 0.f;
+        for (int r = 0; r < 4; ++r) g[r] = fast_exp2(fmaf(acc[i][j][4 * q + r], a.c, -off));
+        if (!full) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if ((int64_t)vt * 256 + vr + r >= a.vrows) g[r] = 0.f;
         }
         u32x2 pk;
         pk[0] = pack_bf16x2(g[0], g[1]);
         pk[1] = pack_bf16x2(g[2], g[3]);
         const int pos = ((vr >> 3) ^ (tl & 31)) * 8 + (vr & 7);
-        *reinterpret_cast<u32x2*>(row(tl) + pos) = pk;
+        *reinterpret_cast<u32x2*>(trow + pos) = pk;
       }
   }
   __syncthreads();
