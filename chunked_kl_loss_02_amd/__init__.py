@@ -11,13 +11,19 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["fwd_bwd", "workspace_size", "lse", "KdProblem", "library_path", "lib",
-           "timing_enable", "timing_collect", "KERNEL_CLASSES", "KD_FLAG_VALIDATE"]
+__all__ = ["fwd_bwd", "fwd", "bwd", "topk_kl_loss", "TopKKLLoss", "workspace_size", "fwd_workspace_size",
+           "saved_size", "lse", "saved_lse", "KdProblem", "library_path", "lib", "timing_enable",
+           "timing_collect", "KERNEL_CLASSES", "KD_FLAG_VALIDATE", "KD_FLAG_ACCUMULATE_DH",
+           "KD_FLAG_ACCUMULATE_DW", "KD_FLAG_GRAD_BF16"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libkdkl.so")
 
 KD_FLAG_VALIDATE = 1
+KD_FLAG_ACCUMULATE_DH = 2
+KD_FLAG_ACCUMULATE_DW = 4
+KD_FLAG_GRAD_BF16 = 8
+ABI_VERSION = 2
 KERNEL_CLASSES = ("teacher", "gather", "pass1", "lse", "loss", "pass2", "fixup", "bwd", "other")
 _STATUS = {0: "KD_OK", 1: "KD_ERR_ARG", 2: "KD_ERR_UNSUPPORTED", 3: "KD_ERR_WORKSPACE",
            4: "KD_ERR_INDEX", 5: "KD_ERR_NONFINITE", 6: "KD_ERR_HIP"}
@@ -53,6 +59,13 @@ def lib():
     L.kd_topk_kl_workspace_size.restype = ctypes.c_int
     L.kd_topk_kl_fwd_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.kd_topk_kl_fwd_bwd.restype = ctypes.c_int
+    for name in ("kd_topk_kl_saved_size", "kd_topk_kl_fwd_workspace_size"):
+        getattr(L, name).argtypes = [P, ctypes.POINTER(sz)]
+        getattr(L, name).restype = ctypes.c_int
+    L.kd_topk_kl_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.kd_topk_kl_fwd.restype = ctypes.c_int
+    L.kd_topk_kl_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.kd_topk_kl_bwd.restype = ctypes.c_int
     L.kd_topk_kl_workspace_lse2.argtypes = [P, vp]
     L.kd_topk_kl_workspace_lse2.restype = vp
     L.kd_status_string.argtypes = [ctypes.c_int]
@@ -63,6 +76,8 @@ def lib():
     L.kd_timing_enable.restype = ctypes.c_int
     L.kd_timing_collect.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
     L.kd_timing_collect.restype = ctypes.c_int
+    if L.kd_abi_version() != ABI_VERSION:
+        raise RuntimeError(f"{library_path} has ABI {L.kd_abi_version()}, this binding expects {ABI_VERSION}: rebuild it")
     _lib = L
     return L
 
@@ -72,32 +87,37 @@ def _raise(code):
         raise KdError(code, lib().kd_status_string(code).decode())
 
 
-def problem(T, H, V, K, tau=1.0, chunk_v=0, block_t=0, validate=False) -> KdProblem:
+def problem(T, H, V, K, tau=1.0, chunk_v=0, block_t=0, validate=False, flags=0) -> KdProblem:
     return KdProblem(int(T), int(H), int(V), int(K), float(tau), int(chunk_v), int(block_t),
-                     KD_FLAG_VALIDATE if validate else 0)
+                     (KD_FLAG_VALIDATE if validate else 0) | int(flags))
 
 
-def workspace_size(T, H, V, K, tau=1.0, chunk_v=0, block_t=0) -> int:
+def _size(fn, prob):
     n = ctypes.c_size_t(0)
-    _raise(lib().kd_topk_kl_workspace_size(ctypes.byref(problem(T, H, V, K, tau, chunk_v, block_t)),
-                                           ctypes.byref(n)))
+    _raise(fn(ctypes.byref(prob), ctypes.byref(n)))
     return n.value
+
+
+def workspace_size(T, H, V, K, tau=1.0, chunk_v=0, block_t=0, flags=0) -> int:
+    """Workspace bytes of fwd_bwd / bwd."""
+    return _size(lib().kd_topk_kl_workspace_size, problem(T, H, V, K, tau, chunk_v, block_t, flags=flags))
+
+
+def fwd_workspace_size(T, H, V, K, tau=1.0, chunk_v=0, block_t=0) -> int:
+    """Workspace bytes of fwd (no gradient buffer)."""
+    return _size(lib().kd_topk_kl_fwd_workspace_size, problem(T, H, V, K, tau, chunk_v, block_t))
+
+
+def saved_size(T, H, V, K, tau=1.0, chunk_v=0, block_t=0) -> int:
+    """Bytes of the state fwd leaves for bwd."""
+    return _size(lib().kd_topk_kl_saved_size, problem(T, H, V, K, tau, chunk_v, block_t))
 
 
 def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
 
 
-def fwd_bwd(h, W, teacher_idx, teacher_logit, mask=None, tau=1.0, *, chunk_v=0, block_t=0,
-            grad_h=True, grad_w=True, row_loss=False, validate=False, workspace=None,
-            return_workspace=False, out=None):
-    """loss, dH, dW [, row_loss] [, workspace] of the fused chunked top-K KL loss.
-
-    h [T,H] bf16, W [V,H] bf16, teacher_idx [T,K] int32, teacher_logit [T,K]
-    fp32, mask [T] uint8/bool or None; all contiguous on the same GPU.  dH and
-    dW are fp32 (None when not requested); loss is a 0-d fp32 tensor.  Runs on
-    torch's current stream; returns without synchronising.  `out` may pass
-    preallocated (loss, dH, dW[, row_loss]) tensors to be overwritten."""
+def _check_inputs(h, W, teacher_idx, teacher_logit, mask):
     import torch
     T, H = h.shape
     V = W.shape[0]
@@ -119,23 +139,62 @@ def fwd_bwd(h, W, teacher_idx, teacher_logit, mask=None, tau=1.0, *, chunk_v=0, 
             mask = mask.view(torch.uint8)
         if mask.dtype != torch.uint8 or mask.shape != (T,) or not mask.is_contiguous() or mask.device != dev:
             raise ValueError("mask must be a contiguous uint8/bool [T] tensor on the same device")
-    prob = problem(T, H, V, K, tau, chunk_v, block_t, validate)
-    n = ctypes.c_size_t(0)
-    _raise(lib().kd_topk_kl_workspace_size(ctypes.byref(prob), ctypes.byref(n)))
-    if workspace is None or workspace.numel() < n.value:
-        workspace = torch.empty(max(n.value, 256), dtype=torch.uint8, device=dev)
+    return T, H, V, K, dev, mask
+
+
+def _grad_flags(grad_dtype, accumulate_dh, accumulate_dw):
+    import torch
+    if grad_dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("gradient outputs are float32 or bfloat16")
+    return ((KD_FLAG_GRAD_BF16 if grad_dtype == torch.bfloat16 else 0)
+            | (KD_FLAG_ACCUMULATE_DH if accumulate_dh else 0) | (KD_FLAG_ACCUMULATE_DW if accumulate_dw else 0))
+
+
+def _check_out(t, shape, dtype, dev, what):
+    if t is not None and (t.dtype != dtype or tuple(t.shape) != tuple(shape) or not t.is_contiguous()
+                          or t.device != dev):
+        raise ValueError(f"{what} must be a contiguous {dtype} tensor of shape {tuple(shape)} on {dev}")
+
+
+def _workspace(workspace, nbytes, dev):
+    import torch
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+    return workspace
+
+
+def fwd_bwd(h, W, teacher_idx, teacher_logit, mask=None, tau=1.0, *, chunk_v=0, block_t=0,
+            grad_h=True, grad_w=True, row_loss=False, validate=False, workspace=None,
+            return_workspace=False, out=None, grad_dtype=None, accumulate_dh=False, accumulate_dw=False):
+    """loss, dH, dW [, row_loss] [, workspace] of the fused chunked top-K KL loss.
+
+    h [T,H] bf16, W [V,H] bf16, teacher_idx [T,K] int32, teacher_logit [T,K]
+    fp32, mask [T] uint8/bool or None; all contiguous on the same GPU.  dH and
+    dW are fp32, or bf16 with grad_dtype=torch.bfloat16 (None when not
+    requested); loss is a 0-d fp32 tensor.  Runs on torch's current stream;
+    returns without synchronising.  `out` may pass preallocated
+    (loss, dH, dW[, row_loss]) tensors, which are overwritten (dH / dW are
+    added to with accumulate_dh / accumulate_dw)."""
+    import torch
+    T, H, V, K, dev, mask = _check_inputs(h, W, teacher_idx, teacher_logit, mask)
+    gdt = grad_dtype or (out[1].dtype if out is not None and out[1] is not None else
+                         out[2].dtype if out is not None and out[2] is not None else torch.float32)
+    flags = _grad_flags(gdt, accumulate_dh, accumulate_dw)
+    prob = problem(T, H, V, K, tau, chunk_v, block_t, validate, flags)
+    workspace = _workspace(workspace, _size(lib().kd_topk_kl_workspace_size, prob), dev)
     if out is not None:
         loss, dH, dW = out[0], out[1], out[2]
         rl = out[3] if row_loss else None
-        for t, shp in ((loss, ()), (dH, (T, H)), (dW, (V, H)), (rl, (T,))):
-            if t is not None and (t.dtype != torch.float32 or tuple(t.shape) != shp or not t.is_contiguous()
-                                  or t.device != dev):
-                raise ValueError("preallocated outputs must be contiguous fp32 of the right shapes")
-        grad_h, grad_w = dH is not None, dW is not None
+        _check_out(loss, (), torch.float32, dev, "loss")
+        _check_out(dH, (T, H), gdt, dev, "dH")
+        _check_out(dW, (V, H), gdt, dev, "dW")
+        _check_out(rl, (T,), torch.float32, dev, "row_loss")
     else:
+        if accumulate_dh or accumulate_dw:
+            raise ValueError("accumulation needs preallocated outputs (out=...)")
         loss = torch.empty((), dtype=torch.float32, device=dev)
-        dH = torch.empty((T, H), dtype=torch.float32, device=dev) if grad_h else None
-        dW = torch.empty((V, H), dtype=torch.float32, device=dev) if grad_w else None
+        dH = torch.empty((T, H), dtype=gdt, device=dev) if grad_h else None
+        dW = torch.empty((V, H), dtype=gdt, device=dev) if grad_w else None
         rl = torch.empty((T,), dtype=torch.float32, device=dev) if row_loss else None
     stream = torch.cuda.current_stream(dev).cuda_stream
     code = lib().kd_topk_kl_fwd_bwd(ctypes.byref(prob), _ptr(h), _ptr(W), _ptr(teacher_idx),
@@ -151,11 +210,113 @@ def fwd_bwd(h, W, teacher_idx, teacher_logit, mask=None, tau=1.0, *, chunk_v=0, 
     return tuple(res)
 
 
-def lse(workspace, T, H, V, K, tau=1.0, chunk_v=0, block_t=0):
+def fwd(h, W, teacher_idx, teacher_logit, mask=None, tau=1.0, *, chunk_v=0, block_t=0, row_loss=False,
+        validate=False, workspace=None):
+    """Loss pass only: (loss, saved[, row_loss]).  `saved` (uint8 device
+    tensor) holds the per-token state bwd needs."""
+    import torch
+    T, H, V, K, dev, mask = _check_inputs(h, W, teacher_idx, teacher_logit, mask)
+    prob = problem(T, H, V, K, tau, chunk_v, block_t, validate)
+    workspace = _workspace(workspace, _size(lib().kd_topk_kl_fwd_workspace_size, prob), dev)
+    saved = torch.empty(_size(lib().kd_topk_kl_saved_size, prob), dtype=torch.uint8, device=dev)
+    loss = torch.empty((), dtype=torch.float32, device=dev)
+    rl = torch.empty((T,), dtype=torch.float32, device=dev) if row_loss else None
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    _raise(lib().kd_topk_kl_fwd(ctypes.byref(prob), _ptr(h), _ptr(W), _ptr(teacher_idx), _ptr(teacher_logit),
+                                _ptr(mask), _ptr(loss), _ptr(rl), _ptr(saved), _ptr(workspace),
+                                ctypes.c_size_t(workspace.numel()), ctypes.c_void_p(stream)))
+    return (loss, saved, rl) if row_loss else (loss, saved)
+
+
+def bwd(saved, h, W, teacher_idx, teacher_logit, mask=None, tau=1.0, *, grad_loss=None, chunk_v=0, block_t=0,
+        grad_h=True, grad_w=True, grad_dtype=None, dH=None, dW=None, accumulate_dh=False, accumulate_dw=False,
+        validate=False, workspace=None):
+    """Gradient pass: (dH, dW) = grad_loss * d(loss)/d(h, W), from the
+    `saved` state of fwd on the same inputs.  grad_loss: 0-d fp32 device
+    tensor or None (= 1).  dH / dW may be preallocated (required to
+    accumulate); their dtype (fp32 or bf16) selects the output type."""
+    import torch
+    T, H, V, K, dev, mask = _check_inputs(h, W, teacher_idx, teacher_logit, mask)
+    gdt = grad_dtype or (dH.dtype if dH is not None else dW.dtype if dW is not None else torch.float32)
+    flags = _grad_flags(gdt, accumulate_dh, accumulate_dw)
+    prob = problem(T, H, V, K, tau, chunk_v, block_t, validate, flags)
+    if saved.dtype != torch.uint8 or saved.device != dev or saved.numel() < _size(lib().kd_topk_kl_saved_size, prob):
+        raise ValueError("saved must be the uint8 state returned by fwd for this problem")
+    if grad_loss is not None:
+        if grad_loss.numel() != 1 or grad_loss.device != dev:
+            raise ValueError("grad_loss must be a one-element tensor on the inputs' device")
+        grad_loss = grad_loss.reshape(()).to(torch.float32).contiguous()
+    if (accumulate_dh and dH is None) or (accumulate_dw and dW is None):
+        raise ValueError("accumulation needs preallocated dH / dW")
+    if dH is None and grad_h:
+        dH = torch.empty((T, H), dtype=gdt, device=dev)
+    if dW is None and grad_w:
+        dW = torch.empty((V, H), dtype=gdt, device=dev)
+    _check_out(dH, (T, H), gdt, dev, "dH")
+    _check_out(dW, (V, H), gdt, dev, "dW")
+    workspace = _workspace(workspace, _size(lib().kd_topk_kl_workspace_size, prob), dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    _raise(lib().kd_topk_kl_bwd(ctypes.byref(prob), _ptr(h), _ptr(W), _ptr(teacher_idx), _ptr(teacher_logit),
+                                _ptr(mask), _ptr(saved), _ptr(grad_loss), _ptr(dH), _ptr(dW), _ptr(workspace),
+                                ctypes.c_size_t(workspace.numel()), ctypes.c_void_p(stream)))
+    return dH, dW
+
+
+def saved_lse(saved, T):
+    """Natural-log per-token log-sum-exp of S/tau from fwd's saved state."""
+    import torch
+    return saved[:4 * T].view(torch.float32) * 0.6931471805599453
+
+
+def _make_autograd():
+    import torch
+
+    class TopKKLLoss(torch.autograd.Function):
+        """Autograd wrapper: forward = fwd, backward = bwd with the incoming
+        gradient as grad_loss; gradients come back in the inputs' dtype
+        (bf16) straight from the library."""
+
+        @staticmethod
+        def forward(ctx, h, W, teacher_idx, teacher_logit, mask, tau, chunk_v, block_t):
+            loss, saved = fwd(h, W, teacher_idx, teacher_logit, mask, tau, chunk_v=chunk_v, block_t=block_t)
+            ctx.save_for_backward(h, W, teacher_idx, teacher_logit, saved,
+                                  mask if mask is not None else torch.empty(0, device=h.device))
+            ctx.has_mask = mask is not None
+            ctx.args = (tau, chunk_v, block_t)
+            return loss
+
+        @staticmethod
+        def backward(ctx, grad):
+            h, W, idx, logit, saved, mask = ctx.saved_tensors
+            tau, chunk_v, block_t = ctx.args
+            need_h, need_w = ctx.needs_input_grad[0], ctx.needs_input_grad[1]
+            dH = dW = None
+            if need_h or need_w:
+                dH, dW = bwd(saved, h, W, idx, logit, mask if ctx.has_mask else None, tau, grad_loss=grad,
+                             chunk_v=chunk_v, block_t=block_t, grad_h=need_h, grad_w=need_w,
+                             grad_dtype=h.dtype)
+            return dH, dW, None, None, None, None, None, None
+
+    return TopKKLLoss
+
+
+TopKKLLoss = None
+
+
+def topk_kl_loss(h, W, teacher_idx, teacher_logit, mask=None, tau=1.0, *, chunk_v=0, block_t=0):
+    """Differentiable fused chunked top-K KL loss (mean over kept tokens);
+    d/dh and d/dW flow back through the library's gradient pass."""
+    global TopKKLLoss
+    if TopKKLLoss is None:
+        TopKKLLoss = _make_autograd()
+    return TopKKLLoss.apply(h, W, teacher_idx, teacher_logit, mask, float(tau), int(chunk_v), int(block_t))
+
+
+def lse(workspace, T, H, V, K, tau=1.0, chunk_v=0, block_t=0, flags=0):
     """Per-token natural-log log-sum-exp of S/tau left in `workspace` by the
     last completed fwd_bwd call with the same problem (fp32 [T] view)."""
     import torch
-    prob = problem(T, H, V, K, tau, chunk_v, block_t)
+    prob = problem(T, H, V, K, tau, chunk_v, block_t, flags=flags)
     addr = lib().kd_topk_kl_workspace_lse2(ctypes.byref(prob), _ptr(workspace))
     if not addr:
         raise KdError(1, "invalid problem")

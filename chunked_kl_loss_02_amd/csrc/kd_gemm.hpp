@@ -254,6 +254,11 @@ __device__ __forceinline__ void wait_all() { asm volatile("s_waitcnt vmcnt(0) lg
 //             whose fragments are already in registers, so the barrier's
 //             bubble is short.
 // On entry a[0], b[0] hold sub-step 0 of (ca, cb); on exit of (na, nb).
+#ifndef KD_VMEM_SPREAD
+#define KD_VMEM_SPREAD 1
+#endif
+constexpr int kVmemSpread = KD_VMEM_SPREAD;
+
 template <int MI, int NI, class LA, class LB>
 __device__ __forceinline__ void kstep(LA& la, LB& lb, int kn, const uint16_t* ca, const uint16_t* cb, uint16_t* na,
                                       uint16_t* nb, f32x16 (&acc)[MI][NI], bf16x8 (&a)[2][MI], bf16x8 (&b)[2][NI],
@@ -261,8 +266,10 @@ __device__ __forceinline__ void kstep(LA& la, LB& lb, int kn, const uint16_t* ca
   constexpr int NM = MI * NI, NR = MI * LA::kReads + NI * LB::kReads;
   constexpr int NVM = LA::kVmem + LB::kVmem, NDSW = LA::kDsw + LB::kDsw;
   static_assert(NR <= NM, "more fragment reads than MFMAs in a sub-step");
-  constexpr int V0 = NVM < NM ? NVM : NM;
-  constexpr int V1 = (NVM - V0) < NM ? (NVM - V0) : NM;
+  // the next stage's loads spread over the first kVmemSpread sub-steps
+  constexpr int per = (NVM + kVmemSpread - 1) / kVmemSpread;
+  constexpr int V0 = NVM < per ? NVM : per;
+  constexpr int V1 = (NVM - V0) < per ? (NVM - V0) : per;
   constexpr int V2 = NVM - V0 - V1;
   static_assert(V2 <= NM, "too many loads for one k-step");
   la.issue(kn, na);

@@ -38,9 +38,13 @@ struct Plan {
   int gm_dh, gm_dw;  // hidden-tile group sizes of the gradient contractions
   int64_t ldp;       // leading dim of the pass-1 partials
   int64_t grows;     // rows of the gradient buffer
-  // workspace offsets (bytes)
-  size_t o_G, o_part, o_lse2, o_p, o_pm, o_s, o_neg, o_row, o_bsum, o_scal_f, o_scal_i, o_status, total;
+  // workspace offsets (bytes); o_G, o_dhs, o_dws are meaningful only in a
+  // plan made with the gradient pass (o_dhs / o_dws: fp32 staging of bf16
+  // gradient outputs)
+  size_t o_G, o_dhs, o_dws, o_part, o_lse2, o_p, o_pm, o_s, o_neg, o_row, o_bsum, o_scal_f, o_scal_i, o_status, total;
 };
+
+constexpr uint32_t kAllFlags = KD_FLAG_VALIDATE | KD_FLAG_ACCUMULATE_DH | KD_FLAG_ACCUMULATE_DW | KD_FLAG_GRAD_BF16;
 
 kd_status check(const kd_problem* p) {
   if (!p) return KD_ERR_ARG;
@@ -48,7 +52,7 @@ kd_status check(const kd_problem* p) {
   if (!(p->tau > 0.f) || !isfinite(p->tau)) return KD_ERR_ARG;
   if ((int64_t)p->K > p->V) return KD_ERR_ARG;
   if (p->chunk_v < 0 || p->block_t < 0) return KD_ERR_ARG;
-  if (p->flags & ~KD_FLAG_VALIDATE) return KD_ERR_ARG;
+  if (p->flags & ~kAllFlags) return KD_ERR_ARG;
   if (p->H % 64 != 0) return KD_ERR_UNSUPPORTED;
   if (p->K > kd::kTeacherMaxK) return KD_ERR_UNSUPPORTED;
   if (p->chunk_v % 256 != 0 || p->block_t % 256 != 0) return KD_ERR_UNSUPPORTED;
@@ -62,7 +66,9 @@ kd_status check(const kd_problem* p) {
   return KD_OK;
 }
 
-Plan make_plan(const kd_problem* p) {
+// Workspace plan.  with_grad: room for the gradient pass (the bf16 gradient
+// tile buffer, and fp32 staging when the gradient outputs are bf16).
+Plan make_plan(const kd_problem* p, bool with_grad = true) {
   Plan P{};
   P.T = p->T;
   P.H = p->H;
@@ -91,7 +97,10 @@ Plan make_plan(const kd_problem* p) {
   const int64_t Tp = align256(P.T);
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t r = o; o += (bytes + 255) & ~size_t(255); return r; };
-  P.o_G = take((size_t)P.grows * P.chunk_v * 2);
+  P.o_G = with_grad ? take((size_t)P.grows * P.chunk_v * 2) : 0;
+  const bool stage = with_grad && (p->flags & KD_FLAG_GRAD_BF16);
+  P.o_dhs = stage ? take((size_t)Tp * P.H * 4) : 0;
+  P.o_dws = stage ? take((size_t)P.chunk_v * P.H * 4) : 0;
   P.o_part = take((size_t)P.nranges * P.ldp * 8);
   P.o_lse2 = take((size_t)Tp * 4);
   P.o_p = take((size_t)P.T * P.K * 4);
@@ -151,11 +160,239 @@ struct Launcher {
 
 int grid_fill(int64_t n, int block) { return (int)std::max<int64_t>(1, std::min<int64_t>(cdiv(n, block), 65536)); }
 
+struct Inputs {
+  const uint16_t* h;
+  const uint16_t* W;
+  const int32_t* idx;
+  const float* logit;
+  const uint8_t* mask;
+};
+
+// Device pointers of one call: workspace regions plus where the saved
+// per-token state (lse2, gathered logits) lives.
+struct Bufs {
+  uint16_t* G;
+  float* dhs;   // fp32 staging of a bf16 dH (nullable)
+  float* dws;   // fp32 staging of one chunk of a bf16 dW (nullable)
+  float2* part;
+  float* lse2;
+  float* p;
+  float* pm;
+  float* s;
+  float* neg;
+  float* rows;
+  double* bsum;
+  float* scal_f;
+  int64_t* scal_i;
+  uint32_t* status;
+};
+
+Bufs carve(const Plan& P, void* workspace, bool with_grad) {
+  char* ws = static_cast<char*>(workspace);
+  Bufs b{};
+  b.G = with_grad ? reinterpret_cast<uint16_t*>(ws + P.o_G) : nullptr;
+  b.dhs = with_grad && P.o_dhs ? reinterpret_cast<float*>(ws + P.o_dhs) : nullptr;
+  b.dws = with_grad && P.o_dws ? reinterpret_cast<float*>(ws + P.o_dws) : nullptr;
+  b.part = reinterpret_cast<float2*>(ws + P.o_part);
+  b.lse2 = reinterpret_cast<float*>(ws + P.o_lse2);
+  b.p = reinterpret_cast<float*>(ws + P.o_p);
+  b.pm = reinterpret_cast<float*>(ws + P.o_pm);
+  b.s = reinterpret_cast<float*>(ws + P.o_s);
+  b.neg = reinterpret_cast<float*>(ws + P.o_neg);
+  b.rows = reinterpret_cast<float*>(ws + P.o_row);
+  b.bsum = reinterpret_cast<double*>(ws + P.o_bsum);
+  b.scal_f = reinterpret_cast<float*>(ws + P.o_scal_f);
+  b.scal_i = reinterpret_cast<int64_t*>(ws + P.o_scal_i);
+  b.status = reinterpret_cast<uint32_t*>(ws + P.o_status);
+  return b;
+}
+
+// The saved state of the split entry points: lse2 [T] then s [T, K].
+size_t saved_lse2_bytes(const Plan& P) { return (size_t)align256(align256(P.T) * 4); }
+size_t saved_bytes(const Plan& P) { return saved_lse2_bytes(P) + (size_t)align256(P.T * P.K * 4) + 256; }
+
+bool misaligned(const void* q, uintptr_t a) { return q && (reinterpret_cast<uintptr_t>(q) & (a - 1)); }
+
+kd_status check_common(const kd_problem* p, const uint16_t* h, const uint16_t* W, const int32_t* idx,
+                       const float* logit, const void* workspace) {
+  const kd_status st = check(p);
+  if (st != KD_OK) return st;
+  if (!W || !workspace) return KD_ERR_ARG;
+  if (p->T > 0 && (!h || !idx || !logit)) return KD_ERR_ARG;
+  if (misaligned(h, 16) || misaligned(W, 16) || misaligned(workspace, 256) || misaligned(idx, 4) ||
+      misaligned(logit, 4))
+    return KD_ERR_UNSUPPORTED;
+  return KD_OK;
+}
+
+// Status clear, N and the gradient coefficient, teacher distribution.
+void launch_prep(Launcher& L, const Plan& P, const Inputs& in, const Bufs& b, bool validate, const float* grad) {
+  hipStream_t s = L.s;
+  using namespace kd;
+  const int64_t T = P.T;
+  if (validate) L.run(8, [&] { k_fill<<<1, 64, 0, s>>>(reinterpret_cast<float*>(b.status), 1, 0.f); });
+  L.run(4, [&] { k_count<<<1, 1024, 0, s>>>(in.mask, T, P.tau, grad, b.scal_f, b.scal_i); });
+  L.run(0, [&] {
+    k_teacher<<<(unsigned)cdiv(T, 4), 256, 0, s>>>(in.idx, in.logit, in.mask, T, P.K, P.V, 1.0f / P.tau, b.p, b.pm,
+                                                    b.neg, b.status, validate ? 1 : 0);
+  });
+}
+
+// Gather, pass 1 (per-token log-sum-exp), per-row loss and the mean.
+void launch_forward(Launcher& L, const Plan& P, const Inputs& in, const Bufs& b, float* loss, float* row_loss) {
+  hipStream_t s = L.s;
+  using namespace kd;
+  const int64_t T = P.T, H = P.H, V = P.V;
+  const int K = P.K;
+  const float c = kLog2e / P.tau;
+  L.run(1, [&] { k_gather<<<(unsigned)T, 256, 0, s>>>(in.h, in.W, in.idx, in.mask, T, H, V, K, b.s); });
+  for (int64_t t0 = 0; t0 < T; t0 += P.Tb) {
+    const int64_t rows = std::min<int64_t>(P.Tb, T - t0);
+    Pass1Args a{};
+    a.W = in.W;
+    a.h = in.h + t0 * H;
+    a.part = b.part;
+    a.V = V;
+    a.H = H;
+    a.rows = rows;
+    a.ntt = (int)cdiv(rows, 256);
+    a.nvt = (int)P.nvt;
+    a.per = P.per;
+    a.nranges = P.nranges;
+    a.gt = std::min(P.gt1, a.ntt);
+    a.gv = std::min(P.gv1, a.nranges);
+    a.total = a.ntt * a.nranges;
+    a.ldp = (int)P.ldp;
+    a.c = c;
+    const int grid = (int)(cdiv(a.total, 8) * 8);
+    L.run(2, [&] { k_pass1<<<grid, 256, 0, s>>>(a); });
+    L.run(3, [&] {
+      k_lse<<<(unsigned)cdiv(rows, 32), 256, 0, s>>>(b.part, P.nranges, (int)P.ldp, rows, b.lse2 + t0);
+    });
+  }
+  const int64_t nb = cdiv(T, 256);
+  float* rows_out = row_loss ? row_loss : b.rows;
+  L.run(4, [&] {
+    k_rows<<<(unsigned)nb, 256, 0, s>>>(b.p, b.s, b.neg, b.lse2, in.mask, T, K, 1.0f / P.tau, rows_out, b.bsum);
+  });
+  L.run(4, [&] { k_sum<<<1, 1024, 0, s>>>(b.bsum, nb, b.scal_f, loss); });
+}
+
+// Pass 2: recompute every (block, chunk), form the logit gradient, contract
+// it into dH / dW (fp32 or bf16 per the flags).
+void launch_backward(Launcher& L, const Plan& P, uint32_t flags, const Inputs& in, const Bufs& b, void* dH_out,
+                     void* dW_out) {
+  hipStream_t s = L.s;
+  using namespace kd;
+  const int64_t T = P.T, H = P.H, V = P.V;
+  const int K = P.K;
+  const float c = kLog2e / P.tau;
+  const bool bf16 = (flags & KD_FLAG_GRAD_BF16) != 0;
+  const bool acc_dh_in = (flags & KD_FLAG_ACCUMULATE_DH) != 0;
+  const bool acc_dw_in = (flags & KD_FLAG_ACCUMULATE_DW) != 0;
+  // fp32 targets of the contractions
+  float* dH = dH_out ? (bf16 ? b.dhs : static_cast<float*>(dH_out)) : nullptr;
+  float* dWc_stage = dW_out && bf16 ? b.dws : nullptr;
+  const int nht = (int)cdiv(H, 256);
+  int ci = 0;
+  for (int64_t v0 = 0; v0 < V; v0 += P.chunk_v, ++ci) {
+    const int64_t vrows = std::min<int64_t>(P.chunk_v, V - v0);
+    const int nvt_c = (int)cdiv(vrows, 256);
+    float* dW = dW_out ? (bf16 ? dWc_stage : static_cast<float*>(dW_out) + v0 * H) : nullptr;
+    int bi = 0;
+    for (int64_t t0 = 0; t0 < T; t0 += P.Tb, ++bi) {
+      const int64_t rows = std::min<int64_t>(P.Tb, T - t0);
+      const int ntt = (int)cdiv(rows, 256);
+      Pass2Args a{};
+      a.W = in.W + v0 * H;
+      a.h = in.h + t0 * H;
+      a.lse2 = b.lse2 + t0;
+      a.mask = in.mask ? in.mask + t0 : nullptr;
+      a.scal_f = b.scal_f;
+      a.G = b.G;
+      a.vrows = vrows;
+      a.H = H;
+      a.rows = rows;
+      a.ntt = ntt;
+      a.nvt = nvt_c;
+      a.gt = std::min(P.gt2, ntt);
+      a.gv = std::min(P.gv2, nvt_c);
+      a.total = ntt * nvt_c;
+      a.ldg = P.chunk_v;
+      a.c = c;
+      const int grid = (int)(cdiv(a.total, 8) * 8);
+      L.run(5, [&] { k_pass2<<<grid, 256, 0, s>>>(a); });
+      L.run(6, [&] {
+        k_fixup<<<(unsigned)cdiv(rows * K, 256), 256, 0, s>>>(in.idx + t0 * K, b.s + t0 * K, b.pm + t0 * K,
+                                                              b.lse2 + t0, in.mask ? in.mask + t0 : nullptr, b.scal_f,
+                                                              rows, K, v0, vrows, c, b.G, P.chunk_v);
+      });
+      BwdArgs g{};
+      g.W = in.W + v0 * H;
+      g.h = in.h + t0 * H;
+      g.G = b.G;
+      g.dH = dH ? dH + t0 * H : nullptr;
+      g.dW = dW;
+      g.vrows = vrows;
+      g.H = H;
+      g.rows = rows;
+      g.nht = nht;
+      g.ntt = ntt;
+      g.nvt = nvt_c;
+      g.ndh = dH ? nht * ntt : 0;
+      g.ndw = dW ? nht * nvt_c : 0;
+      g.ndh_pad = (int)(cdiv(g.ndh, 8) * 8);
+      g.ndw_pad = (int)(cdiv(g.ndw, 8) * 8);
+      g.gm_dh = std::min(P.gm_dh, nht);
+      g.gm_dw = std::min(P.gm_dw, nht);
+      g.ldg = P.chunk_v;
+      g.grows = (int)P.grows;
+      // the first contribution overwrites, later ones add; a caller's
+      // accumulate flag makes every fp32 contribution add (bf16 outputs add
+      // in the final rounding instead)
+      g.acc_dh = ci > 0 || (acc_dh_in && !bf16);
+      g.acc_dw = bi > 0 || (acc_dw_in && !bf16);
+      L.run(7, [&] { k_bwd<<<g.ndh_pad + g.ndw_pad, 256, 0, s>>>(g); });
+    }
+    if (dWc_stage) {
+      const int64_t n = vrows * H;
+      uint16_t* dst = static_cast<uint16_t*>(dW_out) + v0 * H;
+      L.run(8, [&] { k_to_bf16<<<grid_fill(n / 4, 256), 256, 0, s>>>(dWc_stage, dst, n, acc_dw_in ? 1 : 0); });
+    }
+  }
+  if (dH_out && bf16) {
+    const int64_t n = T * H;
+    L.run(8, [&] {
+      k_to_bf16<<<grid_fill(n / 4, 256), 256, 0, s>>>(b.dhs, static_cast<uint16_t*>(dH_out), n, acc_dh_in ? 1 : 0);
+    });
+  }
+}
+
+// Gradient outputs of an empty batch: zero dW (unless accumulating).
+void launch_empty_grads(Launcher& L, const Plan& P, uint32_t flags, void* dW_out) {
+  hipStream_t s = L.s;
+  if (!dW_out || (flags & KD_FLAG_ACCUMULATE_DW)) return;
+  const int64_t words = (flags & KD_FLAG_GRAD_BF16) ? P.V * P.H / 2 : P.V * P.H;
+  L.run(8, [&] { kd::k_fill<<<grid_fill(words, 256), 256, 0, s>>>(static_cast<float*>(dW_out), words, 0.f); });
+}
+
+kd_status finish(Launcher& L, bool validate, const uint32_t* status) {
+  if (L.err != hipSuccess) return KD_ERR_HIP;
+  if (validate) {
+    uint32_t host_status = 0;
+    if (hipMemcpyAsync(&host_status, status, 4, hipMemcpyDeviceToHost, L.s) != hipSuccess) return KD_ERR_HIP;
+    if (hipStreamSynchronize(L.s) != hipSuccess) return KD_ERR_HIP;
+    if (host_status & 1u) return KD_ERR_INDEX;
+    if (host_status & 2u) return KD_ERR_NONFINITE;
+  }
+  return KD_OK;
+}
+
 }  // namespace
 
 extern "C" {
 
-int kd_abi_version(void) { return 1; }
+int kd_abi_version(void) { return 2; }
 
 const char* kd_status_string(kd_status s) {
   switch (s) {
@@ -208,156 +445,94 @@ kd_status kd_timing_collect(double* ms, int64_t* launches) {
 
 kd_status kd_topk_kl_fwd_bwd(const kd_problem* p, const uint16_t* h, const uint16_t* W,
                              const int32_t* teacher_idx, const float* teacher_logit, const uint8_t* mask,
-                             float* loss, float* dH, float* dW, float* row_loss, void* workspace,
+                             float* loss, void* dH, void* dW, float* row_loss, void* workspace,
                              size_t workspace_bytes, void* stream) {
-  const kd_status st = check(p);
+  kd_status st = check_common(p, h, W, teacher_idx, teacher_logit, workspace);
   if (st != KD_OK) return st;
-  if (!W || !loss || !workspace) return KD_ERR_ARG;
-  if (p->T > 0 && (!h || !teacher_idx || !teacher_logit)) return KD_ERR_ARG;
-  auto misaligned = [](const void* q, uintptr_t a) { return q && (reinterpret_cast<uintptr_t>(q) & (a - 1)); };
-  if (misaligned(h, 16) || misaligned(W, 16) || misaligned(dH, 16) || misaligned(dW, 16) ||
-      misaligned(workspace, 256) || misaligned(teacher_idx, 4) || misaligned(teacher_logit, 4) ||
-      misaligned(loss, 4) || misaligned(row_loss, 4))
+  if (!loss) return KD_ERR_ARG;
+  if (misaligned(dH, 16) || misaligned(dW, 16) || misaligned(loss, 4) || misaligned(row_loss, 4))
     return KD_ERR_UNSUPPORTED;
   const Plan P = make_plan(p);
   if (workspace_bytes < P.total) return KD_ERR_WORKSPACE;
-
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  char* ws = static_cast<char*>(workspace);
-  uint16_t* G = reinterpret_cast<uint16_t*>(ws + P.o_G);
-  float2* part = reinterpret_cast<float2*>(ws + P.o_part);
-  float* lse2 = reinterpret_cast<float*>(ws + P.o_lse2);
-  float* tp = reinterpret_cast<float*>(ws + P.o_p);
-  float* tpm = reinterpret_cast<float*>(ws + P.o_pm);
-  float* ts = reinterpret_cast<float*>(ws + P.o_s);
-  float* neg = reinterpret_cast<float*>(ws + P.o_neg);
-  float* rows_out = row_loss ? row_loss : reinterpret_cast<float*>(ws + P.o_row);
-  double* bsum = reinterpret_cast<double*>(ws + P.o_bsum);
-  float* scal_f = reinterpret_cast<float*>(ws + P.o_scal_f);
-  int64_t* scal_i = reinterpret_cast<int64_t*>(ws + P.o_scal_i);
-  uint32_t* status = reinterpret_cast<uint32_t*>(ws + P.o_status);
+  Launcher L{static_cast<hipStream_t>(stream)};
+  const Inputs in{h, W, teacher_idx, teacher_logit, mask};
+  const Bufs b = carve(P, workspace, true);
   const bool validate = (p->flags & KD_FLAG_VALIDATE) != 0;
-  const int64_t T = P.T, H = P.H, V = P.V;
-  const int K = P.K;
-  const float inv_tau = 1.0f / P.tau;
-  const float c = kd::kLog2e / P.tau;
+  if (P.T == 0) {
+    L.run(8, [&] { kd::k_fill<<<1, 64, 0, L.s>>>(loss, 1, 0.f); });
+    launch_empty_grads(L, P, p->flags, dW);
+    return finish(L, false, nullptr);
+  }
+  launch_prep(L, P, in, b, validate, nullptr);
+  launch_forward(L, P, in, b, loss, row_loss);
+  if (dH || dW) launch_backward(L, P, p->flags, in, b, dH, dW);
+  return finish(L, validate, b.status);
+}
 
-  Launcher L{s};
-  using namespace kd;
-  if (T == 0) {
-    L.run(8, [&] { k_fill<<<1, 64, 0, s>>>(loss, 1, 0.f); });
-    if (dW) L.run(8, [&] { k_fill<<<grid_fill(V * H, 256), 256, 0, s>>>(dW, V * H, 0.f); });
-    return L.err == hipSuccess ? KD_OK : KD_ERR_HIP;
-  }
-  if (validate) L.run(8, [&] { k_fill<<<1, 64, 0, s>>>(reinterpret_cast<float*>(status), 1, 0.f); });
-  L.run(4, [&] { k_count<<<1, 1024, 0, s>>>(mask, T, P.tau, scal_f, scal_i); });
-  L.run(0, [&] {
-    k_teacher<<<(unsigned)cdiv(T, 4), 256, 0, s>>>(teacher_idx, teacher_logit, mask, T, K, V, inv_tau, tp, tpm, neg,
-                                                    status, validate ? 1 : 0);
-  });
-  L.run(1, [&] { k_gather<<<(unsigned)T, 256, 0, s>>>(h, W, teacher_idx, mask, T, H, V, K, ts); });
-
-  // pass 1: per-token log-sum-exp over the whole vocabulary, block by block
-  for (int64_t t0 = 0; t0 < T; t0 += P.Tb) {
-    const int64_t rows = std::min<int64_t>(P.Tb, T - t0);
-    kd::Pass1Args a{};
-    a.W = W;
-    a.h = h + t0 * H;
-    a.part = part;
-    a.V = V;
-    a.H = H;
-    a.rows = rows;
-    a.ntt = (int)cdiv(rows, 256);
-    a.nvt = (int)P.nvt;
-    a.per = P.per;
-    a.nranges = P.nranges;
-    a.gt = std::min(P.gt1, a.ntt);
-    a.gv = std::min(P.gv1, a.nranges);
-    a.total = a.ntt * a.nranges;
-    a.ldp = (int)P.ldp;
-    a.c = c;
-    const int grid = (int)(cdiv(a.total, 8) * 8);
-    L.run(2, [&] { k_pass1<<<grid, 256, 0, s>>>(a); });
-    L.run(3, [&] {
-      k_lse<<<(unsigned)cdiv(rows, 32), 256, 0, s>>>(part, P.nranges, (int)P.ldp, rows, lse2 + t0);
-    });
-  }
-  const int64_t nb = cdiv(T, 256);
-  L.run(4, [&] {
-    k_rows<<<(unsigned)nb, 256, 0, s>>>(tp, ts, neg, lse2, mask, T, K, inv_tau, rows_out, bsum);
-  });
-  L.run(4, [&] { k_sum<<<1, 1024, 0, s>>>(bsum, nb, scal_f, loss); });
-
-  // pass 2: recompute every (block, chunk), form the logit gradient, contract it
-  if (dH || dW) {
-    const int nht = (int)cdiv(H, 256);
-    int ci = 0;
-    for (int64_t v0 = 0; v0 < V; v0 += P.chunk_v, ++ci) {
-      const int64_t vrows = std::min<int64_t>(P.chunk_v, V - v0);
-      const int nvt_c = (int)cdiv(vrows, 256);
-      int bi = 0;
-      for (int64_t t0 = 0; t0 < T; t0 += P.Tb, ++bi) {
-        const int64_t rows = std::min<int64_t>(P.Tb, T - t0);
-        const int ntt = (int)cdiv(rows, 256);
-        kd::Pass2Args a{};
-        a.W = W + v0 * H;
-        a.h = h + t0 * H;
-        a.lse2 = lse2 + t0;
-        a.mask = mask ? mask + t0 : nullptr;
-        a.scal_f = scal_f;
-        a.G = G;
-        a.vrows = vrows;
-        a.H = H;
-        a.rows = rows;
-        a.ntt = ntt;
-        a.nvt = nvt_c;
-        a.gt = std::min(P.gt2, ntt);
-        a.gv = std::min(P.gv2, nvt_c);
-        a.total = ntt * nvt_c;
-        a.ldg = P.chunk_v;
-        a.c = c;
-        const int grid = (int)(cdiv(a.total, 8) * 8);
-        L.run(5, [&] { k_pass2<<<grid, 256, 0, s>>>(a); });
-        L.run(6, [&] {
-          k_fixup<<<(unsigned)cdiv(rows * K, 256), 256, 0, s>>>(
-              teacher_idx + t0 * K, ts + t0 * K, tpm + t0 * K, lse2 + t0, mask ? mask + t0 : nullptr, scal_f, rows, K,
-              v0, vrows, c, G, P.chunk_v);
-        });
-        kd::BwdArgs b{};
-        b.W = W + v0 * H;
-        b.h = h + t0 * H;
-        b.G = G;
-        b.dH = dH ? dH + t0 * H : nullptr;
-        b.dW = dW ? dW + v0 * H : nullptr;
-        b.vrows = vrows;
-        b.H = H;
-        b.rows = rows;
-        b.nht = nht;
-        b.ntt = ntt;
-        b.nvt = nvt_c;
-        b.ndh = dH ? nht * ntt : 0;
-        b.ndw = dW ? nht * nvt_c : 0;
-        b.ndh_pad = (int)(cdiv(b.ndh, 8) * 8);
-        b.ndw_pad = (int)(cdiv(b.ndw, 8) * 8);
-        b.gm_dh = std::min(P.gm_dh, nht);
-        b.gm_dw = std::min(P.gm_dw, nht);
-        b.ldg = P.chunk_v;
-        b.grows = (int)P.grows;
-        b.acc_dh = ci > 0;
-        b.acc_dw = bi > 0;
-        L.run(7, [&] { k_bwd<<<b.ndh_pad + b.ndw_pad, 256, 0, s>>>(b); });
-      }
-    }
-  }
-  if (L.err != hipSuccess) return KD_ERR_HIP;
-  if (validate) {
-    uint32_t host_status = 0;
-    if (hipMemcpyAsync(&host_status, status, 4, hipMemcpyDeviceToHost, s) != hipSuccess) return KD_ERR_HIP;
-    if (hipStreamSynchronize(s) != hipSuccess) return KD_ERR_HIP;
-    if (host_status & 1u) return KD_ERR_INDEX;
-    if (host_status & 2u) return KD_ERR_NONFINITE;
-  }
+kd_status kd_topk_kl_saved_size(const kd_problem* p, size_t* bytes) {
+  if (!bytes) return KD_ERR_ARG;
+  const kd_status st = check(p);
+  if (st != KD_OK) return st;
+  *bytes = saved_bytes(make_plan(p, false));
   return KD_OK;
+}
+
+kd_status kd_topk_kl_fwd_workspace_size(const kd_problem* p, size_t* bytes) {
+  if (!bytes) return KD_ERR_ARG;
+  const kd_status st = check(p);
+  if (st != KD_OK) return st;
+  *bytes = make_plan(p, false).total;
+  return KD_OK;
+}
+
+kd_status kd_topk_kl_fwd(const kd_problem* p, const uint16_t* h, const uint16_t* W, const int32_t* teacher_idx,
+                         const float* teacher_logit, const uint8_t* mask, float* loss, float* row_loss, void* saved,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  kd_status st = check_common(p, h, W, teacher_idx, teacher_logit, workspace);
+  if (st != KD_OK) return st;
+  if (!loss || !saved) return KD_ERR_ARG;
+  if (misaligned(saved, 256) || misaligned(loss, 4) || misaligned(row_loss, 4)) return KD_ERR_UNSUPPORTED;
+  const Plan P = make_plan(p, false);
+  if (workspace_bytes < P.total) return KD_ERR_WORKSPACE;
+  Launcher L{static_cast<hipStream_t>(stream)};
+  const Inputs in{h, W, teacher_idx, teacher_logit, mask};
+  Bufs b = carve(P, workspace, false);
+  b.lse2 = static_cast<float*>(saved);
+  b.s = reinterpret_cast<float*>(static_cast<char*>(saved) + saved_lse2_bytes(P));
+  const bool validate = (p->flags & KD_FLAG_VALIDATE) != 0;
+  if (P.T == 0) {
+    L.run(8, [&] { kd::k_fill<<<1, 64, 0, L.s>>>(loss, 1, 0.f); });
+    return finish(L, false, nullptr);
+  }
+  launch_prep(L, P, in, b, validate, nullptr);
+  launch_forward(L, P, in, b, loss, row_loss);
+  return finish(L, validate, b.status);
+}
+
+kd_status kd_topk_kl_bwd(const kd_problem* p, const uint16_t* h, const uint16_t* W, const int32_t* teacher_idx,
+                         const float* teacher_logit, const uint8_t* mask, const void* saved, const float* grad_loss,
+                         void* dH, void* dW, void* workspace, size_t workspace_bytes, void* stream) {
+  kd_status st = check_common(p, h, W, teacher_idx, teacher_logit, workspace);
+  if (st != KD_OK) return st;
+  if (!saved) return KD_ERR_ARG;
+  if (misaligned(saved, 256) || misaligned(dH, 16) || misaligned(dW, 16) || misaligned(grad_loss, 4))
+    return KD_ERR_UNSUPPORTED;
+  const Plan P = make_plan(p);
+  if (workspace_bytes < P.total) return KD_ERR_WORKSPACE;
+  Launcher L{static_cast<hipStream_t>(stream)};
+  const Inputs in{h, W, teacher_idx, teacher_logit, mask};
+  Bufs b = carve(P, workspace, true);
+  b.lse2 = const_cast<float*>(static_cast<const float*>(saved));
+  b.s = reinterpret_cast<float*>(const_cast<char*>(static_cast<const char*>(saved)) + saved_lse2_bytes(P));
+  const bool validate = (p->flags & KD_FLAG_VALIDATE) != 0;
+  if (P.T == 0) {
+    launch_empty_grads(L, P, p->flags, dW);
+    return finish(L, false, nullptr);
+  }
+  if (!dH && !dW) return KD_OK;
+  launch_prep(L, P, in, b, validate, grad_loss);
+  launch_backward(L, P, p->flags, in, b, dH, dW);
+  return finish(L, validate, b.status);
 }
 
 }  // extern "C"

@@ -25,8 +25,11 @@
 namespace kd {
 
 // ----------------------------------------------------------------- small ops
+// N = number of kept tokens; scal_f[0] = g / (N tau) (gradient coefficient,
+// g = *grad or 1), scal_f[1] = 1 / N (0 when N = 0).
 __global__ void __launch_bounds__(1024) k_count(const uint8_t* __restrict__ mask, int64_t T, float tau,
-                                                float* __restrict__ scal_f, int64_t* __restrict__ scal_i) {
+                                                const float* __restrict__ grad, float* __restrict__ scal_f,
+                                                int64_t* __restrict__ scal_i) {
   __shared__ int64_t part[1024];
   int64_t c = 0;
   for (int64_t t = threadIdx.x; t < T; t += 1024) c += mask ? (mask[t] != 0) : 1;
@@ -39,13 +42,35 @@ __global__ void __launch_bounds__(1024) k_count(const uint8_t* __restrict__ mask
   if (threadIdx.x == 0) {
     const int64_t N = part[0];
     scal_i[0] = N;
-    scal_f[0] = N > 0 ? (float)(1.0 / ((double)N * (double)tau)) : 0.0f;  // gradient coefficient
+    const double g = grad ? (double)grad[0] : 1.0;
+    scal_f[0] = N > 0 ? (float)(g / ((double)N * (double)tau)) : 0.0f;  // gradient coefficient
     scal_f[1] = N > 0 ? (float)(1.0 / (double)N) : 0.0f;
   }
 }
 
 __global__ void k_fill(float* __restrict__ p, int64_t n, float v) {
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) p[i] = v;
+}
+
+// dst (bf16) = RNE(src) or RNE(dst + src) (accumulate); n a multiple of 4,
+// both 8-byte aligned.
+__global__ void k_to_bf16(const float* __restrict__ src, uint16_t* __restrict__ dst, int64_t n, int accumulate) {
+  const int64_t n4 = n >> 2;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n4; i += (int64_t)gridDim.x * blockDim.x) {
+    float4 v = reinterpret_cast<const float4*>(src)[i];
+    u32x2* d = reinterpret_cast<u32x2*>(dst) + i;
+    if (accumulate) {
+      const u32x2 o = *d;
+      v.x += __uint_as_float(o[0] << 16);
+      v.y += __uint_as_float(o[0] & 0xFFFF0000u);
+      v.z += __uint_as_float(o[1] << 16);
+      v.w += __uint_as_float(o[1] & 0xFFFF0000u);
+    }
+    u32x2 r;
+    r[0] = pack_bf16x2(v.x, v.y);
+    r[1] = pack_bf16x2(v.z, v.w);
+    *d = r;
+  }
 }
 
 // (m, l) <- (m, l) merged with (om, ol), l = sum 2^(x - m); (-inf, 0) is empty.
@@ -339,8 +364,11 @@ __global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 
   // per-token LSE and gradient coefficient of this lane's 4 token columns,
   // fetched before the K loop so their latency is hidden
   float l2v[4], cfv[4];
+  uint32_t sgn;  // sign bits of a negative coefficient, applied to the packed bf16 pairs
   {
-    const float coef = a.scal_f[0];
+    const float cs = a.scal_f[0];
+    const float coef = fabsf(cs);
+    sgn = cs < 0.f ? 0x80008000u : 0u;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int t = tt * 256 + wn * 128 + acc_col(j, lane);
@@ -359,8 +387,8 @@ __global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 
     uint16_t* b = tl < 64 ? st.a0 : tl < 128 ? st.a1 : tl < 192 ? st.b0 : st.b1;
     return b + (tl & 63) * 256;
   };
-  // G = coef 2^(c S - lse2) = 2^(c S - (lse2 - log2 coef)); a masked or
-  // padding token has coef = 0, i.e. an infinite offset and exact zeros
+  // |G| = |coef| 2^(c S - lse2) = 2^(c S - (lse2 - log2 |coef|)); a masked
+  // or padding token has coef = 0, i.e. an infinite offset and exact zeros
   float offv[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) offv[j] = cfv[j] > 0.f ? l2v[j] - log2f(cfv[j]) : INFINITY;
@@ -384,8 +412,8 @@ __global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 
             if ((int64_t)vt * 256 + vr + r >= a.vrows) g[r] = 0.f;
         }
         u32x2 pk;
-        pk[0] = pack_bf16x2(g[0], g[1]);
-        pk[1] = pack_bf16x2(g[2], g[3]);
+        pk[0] = pack_bf16x2(g[0], g[1]) ^ sgn;
+        pk[1] = pack_bf16x2(g[2], g[3]) ^ sgn;
         const int pos = ((vr >> 3) ^ (tl & 31)) * 8 + (vr & 7);
         *reinterpret_cast<u32x2*>(trow + pos) = pk;
       }

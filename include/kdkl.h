@@ -54,6 +54,16 @@ typedef enum kd_status {
  * valid inputs are a precondition (out-of-range ids never fault: they read
  * zeros and give meaningless results). */
 #define KD_FLAG_VALIDATE 1u
+/* Gradient outputs: add to dH / dW instead of overwriting them (e.g. a
+ * parameter gradient summed over micro-batches). */
+#define KD_FLAG_ACCUMULATE_DH 2u
+#define KD_FLAG_ACCUMULATE_DW 4u
+/* dH and dW are bf16 (bit patterns) instead of fp32.  The contractions still
+ * accumulate in fp32 inside the workspace (dH [T,H] and one chunk of dW,
+ * [chunk_v,H]) and each output element is rounded to bf16 once (to nearest
+ * even), after its last contribution (with an accumulate flag: once, after
+ * adding the previous bf16 value in fp32). */
+#define KD_FLAG_GRAD_BF16 8u
 
 typedef struct kd_problem {
   int64_t T;        /* tokens (rows of h); 0 allowed (loss = 0, dW = 0) */
@@ -66,9 +76,9 @@ typedef struct kd_problem {
   uint32_t flags;   /* KD_FLAG_* */
 } kd_problem;
 
-/* Bytes of device workspace kd_topk_kl_fwd_bwd needs for this problem.
- * Synchronous, host only; returns KD_ERR_ARG / KD_ERR_UNSUPPORTED for a
- * problem the main call would reject. */
+/* Bytes of device workspace kd_topk_kl_fwd_bwd and kd_topk_kl_bwd need for
+ * this problem (flags included).  Synchronous, host only; returns
+ * KD_ERR_ARG / KD_ERR_UNSUPPORTED for a problem the main call would reject. */
 kd_status kd_topk_kl_workspace_size(const kd_problem* p, size_t* bytes);
 
 /* Forward and backward of the loss above, enqueued on `stream`.
@@ -79,8 +89,9 @@ kd_status kd_topk_kl_workspace_size(const kd_problem* p, size_t* bytes);
  *   teacher_logit [T,K]  fp32 cached teacher logits (any per-row shift; -inf = no mass)
  *   mask          [T]    uint8, nonzero = token counts; NULL = all tokens count
  *   loss          [1]    fp32, device, overwritten
- *   dH            [T,H]  fp32, device, 16-byte aligned, overwritten; NULL = not computed
- *   dW            [V,H]  fp32, device, 16-byte aligned, overwritten; NULL = not computed
+ *   dH            [T,H]  fp32 (bf16 with KD_FLAG_GRAD_BF16), device, 16-byte aligned,
+ *                        overwritten (added to with KD_FLAG_ACCUMULATE_DH); NULL = not computed
+ *   dW            [V,H]  as dH (KD_FLAG_ACCUMULATE_DW); NULL = not computed
  *   row_loss      [T]    fp32 mask_t * KL_t (not divided by N), device; NULL = not written
  *   workspace     device memory of at least kd_topk_kl_workspace_size() bytes,
  *                 256-byte aligned; contents on entry are irrelevant
@@ -95,8 +106,42 @@ kd_status kd_topk_kl_fwd_bwd(const kd_problem* p,
                              const uint16_t* h, const uint16_t* W,
                              const int32_t* teacher_idx, const float* teacher_logit,
                              const uint8_t* mask,
-                             float* loss, float* dH, float* dW, float* row_loss,
+                             float* loss, void* dH, void* dW, float* row_loss,
                              void* workspace, size_t workspace_bytes, void* stream);
+
+/* The same loss split into its two passes, for autograd-style callers (the
+ * blog "Making Knowledge Distillation Cheap Enough to Run at Scale", section
+ * "Two systems changes": the forward folds each chunk into the running loss
+ * and discards it; the backward recomputes each chunk).
+ *
+ * kd_topk_kl_fwd runs the loss pass only and leaves in `saved` (caller-owned
+ * device memory of kd_topk_kl_saved_size() bytes, 256-byte aligned) what the
+ * backward needs: the per-token log-sum-exp (fp32 [T] at offset 0, log2
+ * units as in kd_topk_kl_workspace_lse2) followed by the student logits at
+ * the cached teacher ids.  Its workspace is kd_topk_kl_fwd_workspace_size()
+ * bytes (no gradient buffer).  Arguments otherwise as kd_topk_kl_fwd_bwd.
+ *
+ * kd_topk_kl_bwd takes the same problem and inputs plus `saved` from a
+ * kd_topk_kl_fwd call on them, and writes grad_loss * d(loss)/dH and
+ * grad_loss * d(loss)/dW, where grad_loss is an fp32 scalar in device memory
+ * (NULL = 1); the flags KD_FLAG_ACCUMULATE_* and KD_FLAG_GRAD_BF16 apply.
+ * Its workspace is kd_topk_kl_workspace_size() bytes.  `saved` is only
+ * read, so one forward can be followed by several backward calls. */
+kd_status kd_topk_kl_saved_size(const kd_problem* p, size_t* bytes);
+kd_status kd_topk_kl_fwd_workspace_size(const kd_problem* p, size_t* bytes);
+kd_status kd_topk_kl_fwd(const kd_problem* p,
+                         const uint16_t* h, const uint16_t* W,
+                         const int32_t* teacher_idx, const float* teacher_logit,
+                         const uint8_t* mask,
+                         float* loss, float* row_loss, void* saved,
+                         void* workspace, size_t workspace_bytes, void* stream);
+kd_status kd_topk_kl_bwd(const kd_problem* p,
+                         const uint16_t* h, const uint16_t* W,
+                         const int32_t* teacher_idx, const float* teacher_logit,
+                         const uint8_t* mask,
+                         const void* saved, const float* grad_loss,
+                         void* dH, void* dW,
+                         void* workspace, size_t workspace_bytes, void* stream);
 
 /* Device address, inside a workspace used by the last completed call with
  * problem p, of the per-token log-sum-exp of S/tau (natural log would be
@@ -107,7 +152,8 @@ const float* kd_topk_kl_workspace_lse2(const kd_problem* p, const void* workspac
 /* Static message for a status code. */
 const char* kd_status_string(kd_status s);
 
-/* ABI version (incremented on any change of the declarations above). */
+/* ABI version (incremented on any change of the declarations above; 2 adds
+ * the split forward / backward entry points and the gradient flags). */
 int kd_abi_version(void);
 
 /* Optional per-kernel timing with HIP events recorded on the launch stream

@@ -25,7 +25,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("kd_topk_kl_fwd_bwd", "kd_topk_kl_workspace_size", "kd_status_string"):
+    for n in ("kd_topk_kl_fwd_bwd", "kd_topk_kl_workspace_size", "kd_status_string", "kd_topk_kl_fwd",
+              "kd_topk_kl_bwd", "kd_topk_kl_saved_size", "kd_topk_kl_fwd_workspace_size"):
         assert n in names
 
 
@@ -37,7 +38,7 @@ def test_library_exports_every_declared_symbol():
     L = kd.lib()
     for n in declared_functions():
         assert hasattr(L, n)
-    assert L.kd_abi_version() == 1
+    assert L.kd_abi_version() == kd.ABI_VERSION == 2
 
 
 def _ws(T, H, V, K, tau=1.0, chunk_v=0, block_t=0):
@@ -114,3 +115,57 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(kd, "library_path", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError):
         kd.lib()
+
+
+def _size(fn, T, H, V, K, flags=0, chunk_v=0, block_t=0):
+    p = kd.problem(T, H, V, K, 1.0, chunk_v, block_t, flags=flags)
+    n = ctypes.c_size_t(0)
+    code = fn(ctypes.byref(p), ctypes.byref(n))
+    return code, n.value
+
+
+def test_split_entry_point_sizes():
+    L = kd.lib()
+    T, H, V, K = 4096, 2880, 201088, 64
+    code, full = _size(L.kd_topk_kl_workspace_size, T, H, V, K)
+    assert code == 0
+    code, fwd = _size(L.kd_topk_kl_fwd_workspace_size, T, H, V, K)
+    assert code == 0
+    # the forward needs no gradient buffer (4096 x 16384 bf16)
+    assert full - fwd == 4096 * 16384 * 2
+    code, saved = _size(L.kd_topk_kl_saved_size, T, H, V, K)
+    assert code == 0
+    # log-sum-exp [T] and the gathered logits [T, K], fp32, 256-byte aligned pieces
+    assert 4 * T + 4 * T * K <= saved <= 4 * T + 4 * T * K + 1024
+    # bf16 gradient outputs stage fp32 dH [T, H] and one dW chunk [16384, H]
+    code, b16 = _size(L.kd_topk_kl_workspace_size, T, H, V, K, flags=kd.KD_FLAG_GRAD_BF16)
+    assert code == 0
+    assert b16 - full == 4 * T * H + 4 * 16384 * H
+    # accumulate flags change nothing in the plan; unknown flags are rejected
+    assert _size(L.kd_topk_kl_workspace_size, T, H, V, K,
+                 flags=kd.KD_FLAG_ACCUMULATE_DH | kd.KD_FLAG_ACCUMULATE_DW) == (0, full)
+    assert _size(L.kd_topk_kl_workspace_size, T, H, V, K, flags=16)[0] == 1
+    for fn in (L.kd_topk_kl_saved_size, L.kd_topk_kl_fwd_workspace_size):
+        assert _size(fn, T, 2900, V, K)[0] == 2
+
+
+def test_split_entry_points_reject_bad_arguments_before_any_hip_call():
+    L = kd.lib()
+    vp = ctypes.c_void_p
+    p = kd.problem(16, 64, 100, 4)
+    fake = vp(1 << 20)
+    big = ctypes.c_size_t(1 << 30)
+    # fwd: null saved, misaligned saved, small workspace
+    assert L.kd_topk_kl_fwd(ctypes.byref(p), fake, fake, fake, fake, vp(0), fake, vp(0), vp(0), fake, big,
+                            vp(0)) == 1
+    assert L.kd_topk_kl_fwd(ctypes.byref(p), fake, fake, fake, fake, vp(0), fake, vp(0), vp((1 << 20) + 16), fake,
+                            big, vp(0)) == 2
+    assert L.kd_topk_kl_fwd(ctypes.byref(p), fake, fake, fake, fake, vp(0), fake, vp(0), fake, fake,
+                            ctypes.c_size_t(8), vp(0)) == 3
+    # bwd: null saved, misaligned dH, small workspace
+    assert L.kd_topk_kl_bwd(ctypes.byref(p), fake, fake, fake, fake, vp(0), vp(0), vp(0), fake, vp(0), fake, big,
+                            vp(0)) == 1
+    assert L.kd_topk_kl_bwd(ctypes.byref(p), fake, fake, fake, fake, vp(0), fake, vp(0), vp((1 << 20) + 4), vp(0),
+                            fake, big, vp(0)) == 2
+    assert L.kd_topk_kl_bwd(ctypes.byref(p), fake, fake, fake, fake, vp(0), fake, vp(0), fake, vp(0), fake,
+                            ctypes.c_size_t(8), vp(0)) == 3
