@@ -14,7 +14,7 @@ import os
 __all__ = ["fwd_bwd", "fwd", "bwd", "topk_kl_loss", "TopKKLLoss", "workspace_size", "fwd_workspace_size",
            "saved_size", "lse", "saved_lse", "KdProblem", "library_path", "lib", "timing_enable",
            "timing_collect", "KERNEL_CLASSES", "KD_FLAG_VALIDATE", "KD_FLAG_ACCUMULATE_DH",
-           "KD_FLAG_ACCUMULATE_DW", "KD_FLAG_GRAD_BF16"]
+           "KD_FLAG_ACCUMULATE_DW", "KD_FLAG_GRAD_BF16", "KD_FLAG_SEQ_CHUNK"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libkdkl.so")
@@ -23,6 +23,7 @@ KD_FLAG_VALIDATE = 1
 KD_FLAG_ACCUMULATE_DH = 2
 KD_FLAG_ACCUMULATE_DW = 4
 KD_FLAG_GRAD_BF16 = 8
+KD_FLAG_SEQ_CHUNK = 16
 ABI_VERSION = 2
 KERNEL_CLASSES = ("teacher", "gather", "pass1", "lse", "loss", "pass2", "fixup", "bwd", "other")
 _STATUS = {0: "KD_OK", 1: "KD_ERR_ARG", 2: "KD_ERR_UNSUPPORTED", 3: "KD_ERR_WORKSPACE",
@@ -98,8 +99,9 @@ def _size(fn, prob):
     return n.value
 
 
-def workspace_size(T, H, V, K, tau=1.0, chunk_v=0, block_t=0, flags=0) -> int:
+def workspace_size(T, H, V, K, tau=1.0, chunk_v=0, block_t=0, flags=0, seq_chunk=False) -> int:
     """Workspace bytes of fwd_bwd / bwd."""
+    flags |= KD_FLAG_SEQ_CHUNK if seq_chunk else 0
     return _size(lib().kd_topk_kl_workspace_size, problem(T, H, V, K, tau, chunk_v, block_t, flags=flags))
 
 
@@ -165,7 +167,8 @@ def _workspace(workspace, nbytes, dev):
 
 def fwd_bwd(h, W, teacher_idx, teacher_logit, mask=None, tau=1.0, *, chunk_v=0, block_t=0,
             grad_h=True, grad_w=True, row_loss=False, validate=False, workspace=None,
-            return_workspace=False, out=None, grad_dtype=None, accumulate_dh=False, accumulate_dw=False):
+            return_workspace=False, out=None, grad_dtype=None, accumulate_dh=False, accumulate_dw=False,
+            seq_chunk=False):
     """loss, dH, dW [, row_loss] [, workspace] of the fused chunked top-K KL loss.
 
     h [T,H] bf16, W [V,H] bf16, teacher_idx [T,K] int32, teacher_logit [T,K]
@@ -174,12 +177,14 @@ def fwd_bwd(h, W, teacher_idx, teacher_logit, mask=None, tau=1.0, *, chunk_v=0, 
     requested); loss is a 0-d fp32 tensor.  Runs on torch's current stream;
     returns without synchronising.  `out` may pass preallocated
     (loss, dH, dW[, row_loss]) tensors, which are overwritten (dH / dW are
-    added to with accumulate_dh / accumulate_dw)."""
+    added to with accumulate_dh / accumulate_dw).  seq_chunk=True selects the
+    sequence-chunk schedule (stored block logits, no recompute; block_t
+    tokens x V fp32 of workspace)."""
     import torch
     T, H, V, K, dev, mask = _check_inputs(h, W, teacher_idx, teacher_logit, mask)
     gdt = grad_dtype or (out[1].dtype if out is not None and out[1] is not None else
                          out[2].dtype if out is not None and out[2] is not None else torch.float32)
-    flags = _grad_flags(gdt, accumulate_dh, accumulate_dw)
+    flags = _grad_flags(gdt, accumulate_dh, accumulate_dw) | (KD_FLAG_SEQ_CHUNK if seq_chunk else 0)
     prob = problem(T, H, V, K, tau, chunk_v, block_t, validate, flags)
     workspace = _workspace(workspace, _size(lib().kd_topk_kl_workspace_size, prob), dev)
     if out is not None:

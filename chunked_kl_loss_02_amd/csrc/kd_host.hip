@@ -14,6 +14,7 @@ namespace {
 
 constexpr int kDefaultChunkV = 16384;
 constexpr int kDefaultBlockT = 16384;
+constexpr int kDefaultSeqBlockT = 4096;
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
@@ -41,10 +42,13 @@ struct Plan {
   // workspace offsets (bytes); o_G, o_dhs, o_dws are meaningful only in a
   // plan made with the gradient pass (o_dhs / o_dws: fp32 staging of bf16
   // gradient outputs)
+  bool seq;          // sequence-chunk schedule (stored logits of a token block)
+  size_t o_S;        // seq: S^T of one block, [V, Tb] fp32
   size_t o_G, o_dhs, o_dws, o_part, o_lse2, o_p, o_pm, o_s, o_neg, o_row, o_bsum, o_scal_f, o_scal_i, o_status, total;
 };
 
-constexpr uint32_t kAllFlags = KD_FLAG_VALIDATE | KD_FLAG_ACCUMULATE_DH | KD_FLAG_ACCUMULATE_DW | KD_FLAG_GRAD_BF16;
+constexpr uint32_t kAllFlags =
+    KD_FLAG_VALIDATE | KD_FLAG_ACCUMULATE_DH | KD_FLAG_ACCUMULATE_DW | KD_FLAG_GRAD_BF16 | KD_FLAG_SEQ_CHUNK;
 
 kd_status check(const kd_problem* p) {
   if (!p) return KD_ERR_ARG;
@@ -76,7 +80,8 @@ Plan make_plan(const kd_problem* p, bool with_grad = true) {
   P.K = p->K;
   P.tau = p->tau;
   P.chunk_v = p->chunk_v ? p->chunk_v : kDefaultChunkV;
-  P.block_t = p->block_t ? p->block_t : kDefaultBlockT;
+  P.seq = with_grad && (p->flags & KD_FLAG_SEQ_CHUNK);
+  P.block_t = p->block_t ? p->block_t : P.seq ? kDefaultSeqBlockT : kDefaultBlockT;
   P.Tb = P.T < P.block_t ? align256(P.T) : P.block_t;
   if (P.Tb == 0) P.Tb = 256;
   P.ntt_max = (int)(P.Tb / 256);
@@ -98,9 +103,13 @@ Plan make_plan(const kd_problem* p, bool with_grad = true) {
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t r = o; o += (bytes + 255) & ~size_t(255); return r; };
   P.o_G = with_grad ? take((size_t)P.grows * P.chunk_v * 2) : 0;
+  P.o_S = P.seq ? take((size_t)P.V * P.Tb * 4) : 0;
   const bool stage = with_grad && (p->flags & KD_FLAG_GRAD_BF16);
+  // the sequence-chunk schedule finishes a dW chunk only after the last
+  // block: with several blocks its bf16 staging holds all of dW
+  const bool whole_dw = P.seq && P.T > P.Tb;
   P.o_dhs = stage ? take((size_t)Tp * P.H * 4) : 0;
-  P.o_dws = stage ? take((size_t)P.chunk_v * P.H * 4) : 0;
+  P.o_dws = stage ? take((size_t)(whole_dw ? P.V : P.chunk_v) * P.H * 4) : 0;
   P.o_part = take((size_t)P.nranges * P.ldp * 8);
   P.o_lse2 = take((size_t)Tp * 4);
   P.o_p = take((size_t)P.T * P.K * 4);
@@ -265,7 +274,7 @@ void launch_forward(Launcher& L, const Plan& P, const Inputs& in, const Bufs& b,
     a.ldp = (int)P.ldp;
     a.c = c;
     const int grid = (int)(cdiv(a.total, 8) * 8);
-    L.run(2, [&] { k_pass1<<<grid, 256, 0, s>>>(a); });
+    L.run(2, [&] { k_pass1<false><<<grid, 256, 0, s>>>(a); });
     L.run(3, [&] {
       k_lse<<<(unsigned)cdiv(rows, 32), 256, 0, s>>>(b.part, P.nranges, (int)P.ldp, rows, b.lse2 + t0);
     });
@@ -368,6 +377,131 @@ void launch_backward(Launcher& L, const Plan& P, uint32_t flags, const Inputs& i
   }
 }
 
+// Sequence-chunk schedule of kd_topk_kl_fwd_bwd: per token block, pass 1
+// also stores the block's logits; the gradient of each vocabulary chunk is
+// then formed from them (k_sgrad) instead of recomputed, and contracted as in
+// the recompute schedule.  The loss rows are reduced after the last block.
+void launch_seq(Launcher& L, const Plan& P, uint32_t flags, const Inputs& in, const Bufs& b, float* St, float* loss,
+                float* row_loss, void* dH_out, void* dW_out) {
+  hipStream_t s = L.s;
+  using namespace kd;
+  const int64_t T = P.T, H = P.H, V = P.V;
+  const int K = P.K;
+  const float c = kLog2e / P.tau;
+  const bool bf16 = (flags & KD_FLAG_GRAD_BF16) != 0;
+  const bool acc_dh_in = (flags & KD_FLAG_ACCUMULATE_DH) != 0;
+  const bool acc_dw_in = (flags & KD_FLAG_ACCUMULATE_DW) != 0;
+  float* dH = dH_out ? (bf16 ? b.dhs : static_cast<float*>(dH_out)) : nullptr;
+  const bool whole_dw = T > P.Tb;  // bf16 staging holds all of dW
+  const int nht = (int)cdiv(H, 256);
+  const int64_t lds = P.Tb;
+  int bi = 0;
+  for (int64_t t0 = 0; t0 < T; t0 += P.Tb, ++bi) {
+    const int64_t rows = std::min<int64_t>(P.Tb, T - t0);
+    const int ntt = (int)cdiv(rows, 256);
+    Pass1Args a{};
+    a.W = in.W;
+    a.h = in.h + t0 * H;
+    a.part = b.part;
+    a.V = V;
+    a.H = H;
+    a.rows = rows;
+    a.ntt = ntt;
+    a.nvt = (int)P.nvt;
+    a.per = P.per;
+    a.nranges = P.nranges;
+    a.gt = std::min(P.gt1, a.ntt);
+    a.gv = std::min(P.gv1, a.nranges);
+    a.total = a.ntt * a.nranges;
+    a.ldp = (int)P.ldp;
+    a.c = c;
+    a.St = St;
+    a.lds = lds;
+    const int grid = (int)(cdiv(a.total, 8) * 8);
+    L.run(2, [&] { k_pass1<true><<<grid, 256, 0, s>>>(a); });
+    L.run(3, [&] {
+      k_lse<<<(unsigned)cdiv(rows, 32), 256, 0, s>>>(b.part, P.nranges, (int)P.ldp, rows, b.lse2 + t0);
+    });
+    L.run(1, [&] {
+      k_gather_s<<<(unsigned)cdiv(rows * K, 256), 256, 0, s>>>(St, lds, in.idx + t0 * K,
+                                                               in.mask ? in.mask + t0 : nullptr, rows, K, V,
+                                                               b.s + t0 * K);
+    });
+    if (!dH_out && !dW_out) continue;
+    int ci = 0;
+    for (int64_t v0 = 0; v0 < V; v0 += P.chunk_v, ++ci) {
+      const int64_t vrows = std::min<int64_t>(P.chunk_v, V - v0);
+      const int nvt_c = (int)cdiv(vrows, 256);
+      SgradArgs sg{};
+      sg.St = St + v0 * lds;
+      sg.lds = lds;
+      sg.lse2 = b.lse2 + t0;
+      sg.mask = in.mask ? in.mask + t0 : nullptr;
+      sg.scal_f = b.scal_f;
+      sg.G = b.G;
+      sg.vrows = vrows;
+      sg.rows = rows;
+      sg.ldg = P.chunk_v;
+      sg.nvt2 = nvt_c * 2;
+      sg.c = c;
+      L.run(5, [&] { k_sgrad<<<(unsigned)(ntt * 4 * sg.nvt2), 256, 0, s>>>(sg); });
+      L.run(6, [&] {
+        k_fixup<<<(unsigned)cdiv(rows * K, 256), 256, 0, s>>>(in.idx + t0 * K, b.s + t0 * K, b.pm + t0 * K,
+                                                              b.lse2 + t0, in.mask ? in.mask + t0 : nullptr, b.scal_f,
+                                                              rows, K, v0, vrows, c, b.G, P.chunk_v);
+      });
+      float* dW = nullptr;
+      if (dW_out) dW = bf16 ? (whole_dw ? b.dws + v0 * H : b.dws) : static_cast<float*>(dW_out) + v0 * H;
+      BwdArgs g{};
+      g.W = in.W + v0 * H;
+      g.h = in.h + t0 * H;
+      g.G = b.G;
+      g.dH = dH ? dH + t0 * H : nullptr;
+      g.dW = dW;
+      g.vrows = vrows;
+      g.H = H;
+      g.rows = rows;
+      g.nht = nht;
+      g.ntt = ntt;
+      g.nvt = nvt_c;
+      g.ndh = dH ? nht * ntt : 0;
+      g.ndw = dW ? nht * nvt_c : 0;
+      g.ndh_pad = (int)(cdiv(g.ndh, 8) * 8);
+      g.ndw_pad = (int)(cdiv(g.ndw, 8) * 8);
+      g.gm_dh = std::min(P.gm_dh, nht);
+      g.gm_dw = std::min(P.gm_dw, nht);
+      g.ldg = P.chunk_v;
+      g.grows = (int)P.grows;
+      g.acc_dh = ci > 0 || (acc_dh_in && !bf16);
+      g.acc_dw = bi > 0 || (acc_dw_in && !bf16);
+      L.run(7, [&] { k_bwd<<<g.ndh_pad + g.ndw_pad, 256, 0, s>>>(g); });
+      if (dW_out && bf16 && !whole_dw) {
+        const int64_t n = vrows * H;
+        uint16_t* dst = static_cast<uint16_t*>(dW_out) + v0 * H;
+        L.run(8, [&] { k_to_bf16<<<grid_fill(n / 4, 256), 256, 0, s>>>(b.dws, dst, n, acc_dw_in ? 1 : 0); });
+      }
+    }
+  }
+  if (dW_out && bf16 && whole_dw) {
+    const int64_t n = V * H;
+    L.run(8, [&] {
+      k_to_bf16<<<grid_fill(n / 4, 256), 256, 0, s>>>(b.dws, static_cast<uint16_t*>(dW_out), n, acc_dw_in ? 1 : 0);
+    });
+  }
+  if (dH_out && bf16) {
+    const int64_t n = T * H;
+    L.run(8, [&] {
+      k_to_bf16<<<grid_fill(n / 4, 256), 256, 0, s>>>(b.dhs, static_cast<uint16_t*>(dH_out), n, acc_dh_in ? 1 : 0);
+    });
+  }
+  const int64_t nb = cdiv(T, 256);
+  float* rows_out = row_loss ? row_loss : b.rows;
+  L.run(4, [&] {
+    k_rows<<<(unsigned)nb, 256, 0, s>>>(b.p, b.s, b.neg, b.lse2, in.mask, T, K, 1.0f / P.tau, rows_out, b.bsum);
+  });
+  L.run(4, [&] { k_sum<<<1, 1024, 0, s>>>(b.bsum, nb, b.scal_f, loss); });
+}
+
 // Gradient outputs of an empty batch: zero dW (unless accumulating).
 void launch_empty_grads(Launcher& L, const Plan& P, uint32_t flags, void* dW_out) {
   hipStream_t s = L.s;
@@ -464,6 +598,11 @@ kd_status kd_topk_kl_fwd_bwd(const kd_problem* p, const uint16_t* h, const uint1
     return finish(L, false, nullptr);
   }
   launch_prep(L, P, in, b, validate, nullptr);
+  if (P.seq) {
+    float* St = reinterpret_cast<float*>(static_cast<char*>(workspace) + P.o_S);
+    launch_seq(L, P, p->flags, in, b, St, loss, row_loss, dH, dW);
+    return finish(L, validate, b.status);
+  }
   launch_forward(L, P, in, b, loss, row_loss);
   if (dH || dW) launch_backward(L, P, p->flags, in, b, dH, dW);
   return finish(L, validate, b.status);

@@ -189,8 +189,56 @@ struct Pass1Args {
   int64_t V, H, rows;    // rows = valid tokens in the block
   int ntt, nvt, per, nranges, gt, gv, total, ldp;  // gv > 0: group vocabulary ranges instead
   float c;               // log2(e) / tau
+  float* St;             // kStore: S^T of the block, [V rows, lds] fp32 (row v, column t)
+  int64_t lds;
 };
 
+// Writes the raw logits S^T[v, t] of the tile's valid vocabulary rows (the
+// sequence-chunk schedule reads them back instead of recomputing).  The
+// tile leaves in two halves of 128 vocabulary rows through the four free
+// LDS stages (32 rows of 256 fp32 each): the owning waves scatter their
+// accumulators (16-byte chunk c of row r at c ^ 8((r >> 2) & 1), which
+// keeps the two lane halves, 4 rows apart, on different banks), then every
+// thread copies whole 1-KiB row segments to HBM with 16-byte stores.
+__device__ __forceinline__ void store_tile_t(const Pass1Args& a, const Stages& st, const f32x16 (&acc)[4][4], int vt,
+                                             int tt, int wm, int wn, int lane) {
+  auto row = [&](int r) -> float* {
+    uint16_t* b = r < 32 ? st.a0 : r < 64 ? st.a1 : r < 96 ? st.b0 : st.b1;
+    return reinterpret_cast<float*>(b) + (r & 31) * 256;
+  };
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    if (wm == half) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int r = acc_row(i, e, lane);
+          float* rp = row(r);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int t = wn * 128 + acc_col(j, lane);
+            rp[(((t >> 2) ^ (8 * ((r >> 2) & 1))) << 2) | (t & 3)] = acc[i][j][e];
+          }
+        }
+    }
+    __syncthreads();
+    const int64_t v0 = (int64_t)vt * 256 + half * 128;
+#pragma unroll 4
+    for (int k = 0; k < 32; ++k) {
+      const int r = (tid >> 6) + 4 * k, c = tid & 63;
+      if (v0 + r < a.V) {
+        const u32x4 x = *reinterpret_cast<const u32x4*>(row(r) + ((c ^ (8 * ((r >> 2) & 1))) << 2));
+        __builtin_nontemporal_store(x, reinterpret_cast<u32x4*>(a.St + (v0 + r) * a.lds + tt * 256) + c);
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// kStore additionally writes the tile's logits (store_tile_t).
+template <bool kStore>
 __global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) k_pass1(Pass1Args a) {
   KD_DECLARE_STAGES(st, 256, 256);
   __shared__ float2 red[2][128];
@@ -218,6 +266,7 @@ __global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 
     gemm_tile<4, 4>(la, lb, nk, st, acc);
     // vocabulary rows of this lane: vt*256 + wm*128 + acc_row(i, e)
     const int64_t vbase = (int64_t)vt * 256 + wm * 128;
+    if constexpr (kStore) store_tile_t(a, st, acc, vt, tt, wm, wn, lane);
     const bool ragged = vbase + 128 > a.V;
     if (ragged) {
 #pragma unroll
@@ -443,6 +492,77 @@ __global__ void k_fixup(const int32_t* __restrict__ idx, const float* __restrict
   const float q = fast_exp2(fmaf(s[i], c, -lse2[t]));
   const float g = scal_f[0] * (q - pm[i]);
   G[t * ldg + v] = __builtin_bit_cast(uint16_t, (__bf16)g);
+}
+
+// Sequence-chunk schedule: s[t,k] = S[t, idx[t,k]] read from the stored
+// S^T of the block (0 on masked rows), instead of k_gather's dot products.
+__global__ void k_gather_s(const float* __restrict__ St, int64_t lds, const int32_t* __restrict__ idx,
+                           const uint8_t* __restrict__ mask, int64_t rows, int K, int64_t V,
+                           float* __restrict__ s_out) {
+  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (i >= rows * K) return;
+  const int64_t t = i / K;
+  const int32_t v = idx[i];
+  const bool keep = (mask ? mask[t] != 0 : true) && v >= 0 && (int64_t)v < V;
+  s_out[i] = keep ? St[(int64_t)v * lds + t] : 0.f;
+}
+
+// Sequence-chunk schedule: the logit gradient of one (block, chunk) from the
+// stored S^T, G[t, v - v0] = coef_t 2^(c S[v,t] - lse2[t]) in bf16, zero for
+// masked / padding tokens and vocabulary rows past V; the whole padded tile
+// grid of the chunk is written, as k_pass2 does.  A workgroup transposes a
+// 128 (vocabulary) x 64 (token) tile through LDS: coalesced fp32 reads along
+// tokens, coalesced bf16 writes along the vocabulary.  LDS rows are 65 words
+// (one bank of skew per token row) so both LDS phases are conflict-free.
+struct SgradArgs {
+  const float* St;        // block's S^T, row v0 origin: [*, lds]
+  int64_t lds;
+  const float* lse2;      // block origin
+  const uint8_t* mask;    // block origin (nullable)
+  const float* scal_f;
+  uint16_t* G;            // [*, ldg]
+  int64_t vrows, rows;    // valid vocabulary rows in the chunk / tokens in the block
+  int ldg, nvt2;          // nvt2 = vocabulary tiles of 128 in the padded chunk
+  float c;
+};
+
+__global__ void __launch_bounds__(256) k_sgrad(SgradArgs a) {
+  __shared__ uint32_t tile[64 * 65];
+  const int vt = blockIdx.x % a.nvt2, ttile = blockIdx.x / a.nvt2;
+  const int th = threadIdx.x;
+  const int q = th & 15;               // 4 tokens: 4q .. 4q+3
+  const int64_t t0 = (int64_t)ttile * 64;
+  const float cf = a.scal_f[0];
+  float l2[4];
+  bool tv[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int64_t t = t0 + 4 * q + k;
+    tv[k] = t < a.rows && (a.mask ? a.mask[t] != 0 : true);
+    l2[k] = tv[k] ? a.lse2[t] : 0.f;
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int pr = (th >> 4) + 16 * r;  // row pair 0..63: vocabulary rows 2pr, 2pr+1
+    const int64_t v = (int64_t)vt * 128 + 2 * pr;
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    f32x4 x0 = {0.f, 0.f, 0.f, 0.f}, x1 = x0;
+    if (v < a.vrows) x0 = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(a.St + v * a.lds + t0) + q);
+    if (v + 1 < a.vrows) x1 = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(a.St + (v + 1) * a.lds + t0) + q);
+    const float s0[4] = {x0[0], x0[1], x0[2], x0[3]}, s1[4] = {x1[0], x1[1], x1[2], x1[3]};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float g0 = tv[k] && v < a.vrows ? cf * fast_exp2(fmaf(s0[k], a.c, -l2[k])) : 0.f;
+      const float g1 = tv[k] && v + 1 < a.vrows ? cf * fast_exp2(fmaf(s1[k], a.c, -l2[k])) : 0.f;
+      tile[(4 * q + k) * 65 + pr] = pack_bf16x2(g0, g1);
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int tl = (th >> 6) + 4 * r, wd = th & 63;
+    reinterpret_cast<uint32_t*>(a.G + (t0 + tl) * a.ldg + (int64_t)vt * 128)[wd] = tile[tl * 65 + wd];
+  }
 }
 
 // dH (over the chunk's vocabulary) and dW (over the block's tokens) from G.

@@ -64,6 +64,15 @@ typedef enum kd_status {
  * even), after its last contribution (with an accumulate flag: once, after
  * adding the previous bf16 value in fp32). */
 #define KD_FLAG_GRAD_BF16 8u
+/* kd_topk_kl_fwd_bwd only: the sequence-chunk schedule of the blog "Making
+ * Knowledge Distillation Cheap Enough to Run at Scale" (section "Two systems
+ * changes": one chunk of the sequence at a time).  The forward pass keeps a
+ * token block's logits (fp32, block_t x V, in the workspace) and the backward
+ * forms the logit gradient from them instead of recomputing the projection:
+ * 6 T H V instead of 8 T H V flops, for block_t * V * 4 bytes of workspace
+ * (block_t = 0 means 4096 here).  Same results up to fp32 rounding order.
+ * kd_topk_kl_fwd / kd_topk_kl_bwd ignore it. */
+#define KD_FLAG_SEQ_CHUNK 16u
 
 typedef struct kd_problem {
   int64_t T;        /* tokens (rows of h); 0 allowed (loss = 0, dW = 0) */

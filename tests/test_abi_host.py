@@ -144,7 +144,12 @@ def test_split_entry_point_sizes():
     # accumulate flags change nothing in the plan; unknown flags are rejected
     assert _size(L.kd_topk_kl_workspace_size, T, H, V, K,
                  flags=kd.KD_FLAG_ACCUMULATE_DH | kd.KD_FLAG_ACCUMULATE_DW) == (0, full)
-    assert _size(L.kd_topk_kl_workspace_size, T, H, V, K, flags=16)[0] == 1
+    assert _size(L.kd_topk_kl_workspace_size, T, H, V, K, flags=32)[0] == 1
+    # the sequence-chunk schedule keeps one token block of fp32 logits (block 4096 by default)
+    code, sq = _size(L.kd_topk_kl_workspace_size, T, H, V, K, flags=kd.KD_FLAG_SEQ_CHUNK)
+    assert code == 0 and sq - full == 4 * V * 4096
+    assert _size(L.kd_topk_kl_workspace_size, T, H, V, K, flags=kd.KD_FLAG_SEQ_CHUNK, block_t=1024)[1] - \
+        _size(L.kd_topk_kl_workspace_size, T, H, V, K, block_t=1024)[1] == 4 * V * 1024
     for fn in (L.kd_topk_kl_saved_size, L.kd_topk_kl_fwd_workspace_size):
         assert _size(fn, T, 2900, V, K)[0] == 2
 

@@ -38,12 +38,12 @@ def sample_rows(T, n, seed):
     return np.sort(np.random.default_rng(seed).choice(T, size=min(n, T), replace=False))
 
 
-def protocol_i(wl, n_rows=128, seed=7):
-    print(f"[full-i] {wl}", flush=True)
+def protocol_i(wl, n_rows=128, seed=7, seq_chunk=False):
+    print(f"[full-i] {wl} seq_chunk={seq_chunk}", flush=True)
     x = synth.make_inputs_torch(wl.T, wl.H, wl.V, wl.K, seed=3, mask=wl.mask)
     loss, dH, dW, rl, ws = kd.fwd_bwd(x["h"], x["W"], x["teacher_idx"], x["teacher_logit"], x["mask"], wl.tau,
-                                      grad_w=False, row_loss=True, return_workspace=True)
-    lse = kd.lse(ws, wl.T, wl.H, wl.V, wl.K, wl.tau)
+                                      grad_w=False, row_loss=True, return_workspace=True, seq_chunk=seq_chunk)
+    lse = kd.lse(ws, wl.T, wl.H, wl.V, wl.K, wl.tau, flags=kd.KD_FLAG_SEQ_CHUNK if seq_chunk else 0)
     torch.cuda.synchronize()
     rows = sample_rows(wl.T, n_rows, seed)
     s = host(x, rows)
@@ -68,14 +68,14 @@ def protocol_i(wl, n_rows=128, seed=7):
     assert torch.all(torch.isfinite(dH)).item()
 
 
-def protocol_ii(wl, n_rows=128, seed=11):
-    print(f"[full-ii] {wl}", flush=True)
+def protocol_ii(wl, n_rows=128, seed=11, seq_chunk=False):
+    print(f"[full-ii] {wl} seq_chunk={seq_chunk}", flush=True)
     x = synth.make_inputs_torch(wl.T, wl.H, wl.V, wl.K, seed=5, mask=wl.mask)
     rows = sample_rows(wl.T, n_rows, seed)
     keep = torch.zeros(wl.T, dtype=torch.uint8, device="cuda")
     keep[torch.from_numpy(rows).cuda()] = 1
     m2 = (x["mask"] * keep).contiguous()
-    loss, dH, dW = kd.fwd_bwd(x["h"], x["W"], x["teacher_idx"], x["teacher_logit"], m2, wl.tau)
+    loss, dH, dW = kd.fwd_bwd(x["h"], x["W"], x["teacher_idx"], x["teacher_logit"], m2, wl.tau, seq_chunk=seq_chunk)
     torch.cuda.synchronize()
     s = host(x, rows)
     s["mask"] = m2.index_select(0, torch.from_numpy(rows).cuda()).cpu().numpy()
@@ -103,6 +103,19 @@ def test_gptoss_full_mask_rows():
 
 def test_gptoss_restricted_mask_full_grads():
     protocol_ii(synth.WORKLOADS["gptoss"])
+
+
+def test_gptoss_seq_chunk_full_mask_rows():
+    protocol_i(synth.WORKLOADS["gptoss"], seq_chunk=True)
+
+
+def test_gptoss_seq_chunk_restricted_mask_full_grads():
+    protocol_ii(synth.WORKLOADS["gptoss"], seq_chunk=True)
+
+
+def test_long_context_seq_chunk_rows():
+    # 8 blocks of 4096 tokens
+    protocol_i(synth.WORKLOADS["long"], seq_chunk=True)
 
 
 def test_long_context_packed_rows():

@@ -22,6 +22,22 @@ pytestmark = pytest.mark.gpu
 LOSS_TOL = 1e-3
 GRAD_TOL = 2e-2
 
+# every case runs under both schedules of the fused call: recompute (pass 2
+# recomputes each chunk's logits) and sequence-chunk (a token block's logits
+# are stored by pass 1 and reused)
+SEQ = False
+
+
+@pytest.fixture(autouse=True, params=["recompute", "seq_chunk"])
+def schedule(request):
+    global SEQ
+    SEQ = request.param == "seq_chunk"
+    yield
+
+
+def fb(*args, **kw):
+    return kd.fwd_bwd(*args, seq_chunk=SEQ, **kw)
+
 
 def to_dev(x, dev="cuda"):
     h = torch.from_numpy(x["h_bits"].view(np.int16)).view(torch.bfloat16).to(dev)
@@ -39,9 +55,9 @@ def nrel(a, b):
 
 def run_case(x, tau, **kw):
     print(f"[case] T={x['h'].shape[0]} H={x['h'].shape[1]} V={x['W'].shape[0]} K={x['teacher_idx'].shape[1]} "
-          f"tau={tau} {kw}", flush=True)
+          f"tau={tau} {kw} seq={SEQ}", flush=True)
     h, W, idx, lg, m = to_dev(x)
-    loss, dH, dW, rl = kd.fwd_bwd(h, W, idx, lg, m, tau, row_loss=True, **kw)
+    loss, dH, dW, rl = fb(h, W, idx, lg, m, tau, row_loss=True, **kw)
     torch.cuda.synchronize()
     ref = kl_dense(x["h"], x["W"], x["teacher_idx"], x["teacher_logit"], x["mask"], tau)
     got = dict(loss=loss.item(), dH=dH.cpu().double().numpy(), dW=dW.cpu().double().numpy(),
@@ -149,7 +165,7 @@ def test_empty_sequence():
     h = torch.empty(0, 64, device="cuda", dtype=torch.bfloat16)
     idx = torch.empty(0, 4, device="cuda", dtype=torch.int32)
     lg = torch.empty(0, 4, device="cuda", dtype=torch.float32)
-    loss, dH, dW = kd.fwd_bwd(h, W, idx, lg, None, 1.0)
+    loss, dH, dW = fb(h, W, idx, lg, None, 1.0)
     torch.cuda.synchronize()
     assert loss.item() == 0.0 and dH.numel() == 0 and not torch.any(dW)
 
@@ -157,10 +173,10 @@ def test_empty_sequence():
 def test_loss_only_and_single_gradient_modes():
     x = make(160, 128, 1500, 8, 10)
     h, W, idx, lg, m = to_dev(x)
-    full = kd.fwd_bwd(h, W, idx, lg, m, 1.0)
-    lo = kd.fwd_bwd(h, W, idx, lg, m, 1.0, grad_h=False, grad_w=False)
-    oh = kd.fwd_bwd(h, W, idx, lg, m, 1.0, grad_w=False)
-    ow = kd.fwd_bwd(h, W, idx, lg, m, 1.0, grad_h=False)
+    full = fb(h, W, idx, lg, m, 1.0)
+    lo = fb(h, W, idx, lg, m, 1.0, grad_h=False, grad_w=False)
+    oh = fb(h, W, idx, lg, m, 1.0, grad_w=False)
+    ow = fb(h, W, idx, lg, m, 1.0, grad_h=False)
     torch.cuda.synchronize()
     assert lo[0].item() == full[0].item()
     assert torch.equal(oh[1], full[1]) and torch.equal(ow[2], full[2])
@@ -169,9 +185,9 @@ def test_loss_only_and_single_gradient_modes():
 def test_deterministic_and_chunk_invariant_loss():
     x = make(300, 256, 5000, 16, 11)
     h, W, idx, lg, m = to_dev(x)
-    a = kd.fwd_bwd(h, W, idx, lg, m, 1.0, chunk_v=1024)
-    b = kd.fwd_bwd(h, W, idx, lg, m, 1.0, chunk_v=1024)
-    c = kd.fwd_bwd(h, W, idx, lg, m, 1.0, chunk_v=256, block_t=256)
+    a = fb(h, W, idx, lg, m, 1.0, chunk_v=1024)
+    b = fb(h, W, idx, lg, m, 1.0, chunk_v=1024)
+    c = fb(h, W, idx, lg, m, 1.0, chunk_v=256, block_t=256)
     torch.cuda.synchronize()
     for u, v in zip(a, b):
         assert torch.equal(u, v)  # bitwise run-to-run
@@ -182,9 +198,9 @@ def test_deterministic_and_chunk_invariant_loss():
 def test_lse_matches_oracle():
     x = make(128, 256, 4096, 32, 12)
     h, W, idx, lg, m = to_dev(x)
-    out = kd.fwd_bwd(h, W, idx, lg, m, 1.5, return_workspace=True)
+    out = fb(h, W, idx, lg, m, 1.5, return_workspace=True)
     torch.cuda.synchronize()
-    lse = kd.lse(out[-1], 128, 256, 4096, 32, 1.5).cpu().double().numpy()
+    lse = kd.lse(out[-1], 128, 256, 4096, 32, 1.5, flags=kd.KD_FLAG_SEQ_CHUNK if SEQ else 0).cpu().double().numpy()
     ref = kl_dense(x["h"], x["W"], x["teacher_idx"], x["teacher_logit"], x["mask"], 1.5, grads=False)
     assert np.max(np.abs(lse - ref["lse"])) < 1e-4
 
@@ -192,18 +208,45 @@ def test_lse_matches_oracle():
 def test_validation_flag_reports_bad_teacher_data():
     x = make(64, 64, 500, 4, 13)
     h, W, idx, lg, m = to_dev(x)
-    kd.fwd_bwd(h, W, idx, lg, m, 1.0, validate=True)  # clean inputs pass
+    fb(h, W, idx, lg, m, 1.0, validate=True)  # clean inputs pass
     bad = idx.clone()
     bad[7, 2] = 500
     with pytest.raises(kd.KdError) as e:
-        kd.fwd_bwd(h, W, bad, lg, m, 1.0, validate=True)
+        fb(h, W, bad, lg, m, 1.0, validate=True)
     assert e.value.code == 4
     badl = lg.clone()
     badl[3, 0] = float("nan")
     with pytest.raises(kd.KdError) as e:
-        kd.fwd_bwd(h, W, idx, badl, m, 1.0, validate=True)
+        fb(h, W, idx, badl, m, 1.0, validate=True)
     assert e.value.code == 5
     # a masked row's teacher data is never inspected
     m2 = m.clone()
     m2[3] = 0
-    kd.fwd_bwd(h, W, idx, badl, m2, 1.0, validate=True)
+    fb(h, W, idx, badl, m2, 1.0, validate=True)
+
+
+def test_schedules_agree():
+    """Both schedules compute the same S tiles with the same engine; the
+    gradient buffers differ only in fp32 rounding order of the exponent, so
+    loss and gradients agree far inside the oracle tolerances."""
+    x = make(700, 128, 3000, 16, 14, mask="pad10")
+    h, W, idx, lg, m = to_dev(x)
+    a = kd.fwd_bwd(h, W, idx, lg, m, 1.3, chunk_v=512, block_t=256, row_loss=True)
+    b = kd.fwd_bwd(h, W, idx, lg, m, 1.3, chunk_v=512, block_t=256, row_loss=True, seq_chunk=True)
+    torch.cuda.synchronize()
+    assert abs(a[0].item() - b[0].item()) <= 1e-6 * abs(a[0].item())
+    assert torch.allclose(a[3], b[3], rtol=1e-5, atol=1e-6)
+    for u, v in ((a[1], b[1]), (a[2], b[2])):
+        assert (torch.linalg.norm(u - v) / torch.linalg.norm(u)).item() < 2e-3
+
+
+def test_seq_chunk_bf16_gradients_over_several_blocks():
+    """Sequence-chunk schedule with bf16 outputs and several token blocks:
+    dW is staged whole in fp32 and rounded once."""
+    x = make(700, 128, 3000, 16, 15)
+    h, W, idx, lg, m = to_dev(x)
+    _, dH, dW = kd.fwd_bwd(h, W, idx, lg, m, 1.0, chunk_v=512, block_t=256, seq_chunk=True)
+    _, bH, bW = kd.fwd_bwd(h, W, idx, lg, m, 1.0, chunk_v=512, block_t=256, seq_chunk=True,
+                           grad_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(bH, dH.to(torch.bfloat16)) and torch.equal(bW, dW.to(torch.bfloat16))
