@@ -4,7 +4,9 @@
 
 One step = one kd_topk_kl_fwd_bwd call (teacher prep, gather, pass 1
 log-sum-exp, loss, pass 2 recompute + logit gradient + dH/dW contractions)
-over one synthetic batch already resident in HBM.  Prints one JSON line.
+over one synthetic batch already resident in HBM.  Prints one JSON line;
+its "seq_chunk" object times the same call under the sequence-chunk
+schedule (stored block logits instead of the pass-2 recompute).
 
 Other modes (not the benchmark line):
   --copy-probe      a plain device copy of known size, to calibrate rocprofv3
@@ -88,6 +90,54 @@ def load_traffic(launch_flops):
     if d.get("kernel_source_hash") != kernel_source_hash():
         return None
     return d.get("hbm_bytes_per_launch")
+
+
+def run_seq_chunk(args, wl, x):
+    """The sequence-chunk schedule on the same inputs: pass 1 keeps a token
+    block's logits (fp32, in the workspace) and the gradient is formed from
+    them, 6 T H V flops instead of 8.  Reported beside the main line."""
+    import torch
+    import chunked_kl_loss_02_amd as kd
+    dev = x["h"].device
+    T, H, V, K, tau = wl.T, wl.H, wl.V, wl.K, wl.tau
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    ws_bytes = kd.workspace_size(T, H, V, K, tau, seq_chunk=True)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    outs = (torch.empty((), dtype=torch.float32, device=dev),
+            torch.empty((T, H), dtype=torch.float32, device=dev),
+            torch.empty((V, H), dtype=torch.float32, device=dev))
+
+    def step():
+        return kd.fwd_bwd(x["h"], x["W"], x["teacher_idx"], x["teacher_logit"], x["mask"], tau,
+                          workspace=ws, out=outs, seq_chunk=True)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats(dev)
+    kd.timing_enable(True)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    kd.timing_enable(False)
+    per_kernel = kd.timing_collect()
+    peak = torch.cuda.max_memory_allocated(dev)
+    bwd_ms, bwd_n = per_kernel["bwd"]
+    res = {
+        "value": T * args.steps / dt, "unit": "tokens/s", "ms_per_step": dt * 1e3 / args.steps,
+        "flops_per_token": 6.0 * H * V,
+        "tflops": 6.0 * H * V * T * args.steps / dt / 1e12,
+        "bwd_achieved_tflops": 4.0 * T * H * V * args.steps / (bwd_ms * 1e-3) / 1e12 if bwd_ms > 0 else 0.0,
+        "per_kernel_ms_per_step": {k: v[0] / args.steps for k, v in per_kernel.items() if v[1]},
+        "peak_mem_bytes": int(peak), "workspace_bytes": int(ws_bytes),
+        "loss": outs[0].item(),
+    }
+    del ws, outs
+    torch.cuda.empty_cache()
+    return res
 
 
 def run_one(args, wl):
@@ -183,6 +233,7 @@ def main():
     ap.add_argument("--seed", type=int, default=1)
     ap.add_argument("--workload", default="gptoss", choices=["gptoss", "long", "qwen", "tiny"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-seq-chunk", action="store_true", help="skip the sequence-chunk schedule line")
     ap.add_argument("--cpu-rows", type=int, default=2048)
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--sweep", action="store_true")
@@ -205,6 +256,9 @@ def main():
         return
     wl = synth.WORKLOADS[args.workload]
     res, x = run_one(args, wl)
+    res["config"]["schedule"] = "recompute (pass 2 recomputes each vocabulary chunk)"
+    if not args.no_seq_chunk:
+        res["seq_chunk"] = run_seq_chunk(args, wl, x)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(x, wl.tau, args.cpu_rows)
     else:

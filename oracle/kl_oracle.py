@@ -43,7 +43,7 @@ import math
 import numpy as np
 
 __all__ = ["teacher_distribution", "teacher_on_vocab", "student_log_softmax",
-           "kl_dense", "kl_sparse", "kl_chunked", "kl_loops"]
+           "kl_dense", "kl_sparse", "kl_chunked", "kl_loops", "kl_logits", "topk_rows"]
 
 
 def _f64(x):
@@ -254,3 +254,51 @@ def kl_loops(h, W, teacher_idx, teacher_logit, mask=None, tau=1.0):
     dW = [[math.fsum(G[t][v] * h[t][i] for t in range(T)) for i in range(H)] for v in range(V)]
     return dict(loss=loss, row_loss=np.array(row_loss), kl=np.array(kl),
                 dH=np.array(dH).reshape(T, H), dW=np.array(dW).reshape(V, H), N=N)
+
+
+def kl_logits(Z, teacher_idx, teacher_logit, mask=None, tau=1.0, grads=True):
+    """Forward-chunked KL on already materialised student logits Z[T,V] (page
+    "Making Knowledge Distillation Cheap Enough to Run at Scale", "Two systems
+    changes", second variant: the teacher stays sparse, the student's logits
+    exist in full).  Same loss as kl_dense with S replaced by Z; the gradient
+    is with respect to the logits: dZ[t,v] = mask_t/(N tau) (q[t,v] - P[t,v]).
+
+    Returns loss, row_loss, kl, lse (natural log of sum exp(Z/tau)), N and,
+    if grads, dZ [T,V] (float64)."""
+    Z = _f64(Z)
+    T, V = Z.shape
+    m = _mask(mask, T)
+    N = int(np.sum(m))
+    logq, lse = student_log_softmax(Z, tau)
+    p = teacher_distribution(teacher_logit, tau)
+    P = teacher_on_vocab(teacher_idx, p, V)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        plogp = np.where(P > 0, P * np.log(np.where(P > 0, P, 1.0)), 0.0)
+    kl = np.sum(plogp, axis=1) - np.sum(P * logq, axis=1)
+    row_loss = np.where(m, kl, 0.0)
+    loss = float(np.sum(row_loss) / N) if N > 0 else 0.0
+    out = dict(loss=loss, row_loss=row_loss, kl=kl, lse=lse, N=N)
+    if grads:
+        coef = np.where(m, 1.0 / (N * float(tau)) if N > 0 else 0.0, 0.0)
+        dZ = coef[:, None] * (np.exp(logq) - P)
+        dZ[~m] = 0.0
+        out["dZ"] = dZ
+    return out
+
+
+def topk_rows(X, K):
+    """The teacher cache's content (page "Making Knowledge Distillation Cheap
+    Enough to Run at Scale", "Two systems changes": the K most likely tokens
+    per position are cached): for every row of X[T,V], the ids of its K
+    largest values in descending order of value, equal values by ascending
+    id, and those values.  Returns (idx int64 [T,K], values float64 [T,K])."""
+    X = np.asarray(X)
+    T, V = X.shape
+    K = int(K)
+    ids = np.arange(V)
+    idx = np.empty((T, K), dtype=np.int64)
+    for t in range(T):
+        order = np.lexsort((ids, -X[t].astype(np.float64)))
+        idx[t] = order[:K]
+    vals = np.take_along_axis(X.astype(np.float64), idx, axis=1)
+    return idx, vals

@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import (kl_dense, kl_sparse, kl_chunked, kl_loops,
+from oracle import (kl_dense, kl_sparse, kl_chunked, kl_loops, kl_logits, topk_rows,
                     teacher_distribution)
 
 
@@ -305,3 +305,99 @@ def test_teacher_distribution_softmax_library():
     assert np.max(np.abs(p - ref)) < 1e-15
     assert np.allclose(p.sum(1), 1.0, atol=1e-15)
     assert p[1, 2] == 0.0
+
+
+# ------------------------------------------------ forward-chunked (given logits)
+@pytest.mark.parametrize("tau,K", [(1.0, 5), (2.5, 17)])
+def test_kl_logits_matches_torch_kl_div_and_autograd(tau, K):
+    """Loss on given student logits Z against torch fp64 log_softmax + kl_div,
+    and dZ against torch autograd with respect to Z."""
+    T, V = 9, 60
+    r = np.random.default_rng(40 + K)
+    Z = r.standard_normal((T, V)) * 3.0
+    idx = np.stack([r.choice(V, K, replace=False) for _ in range(T)]).astype(np.int32)
+    logit = r.standard_normal((T, K)) * 2.0
+    mask = np.ones(T, np.uint8)
+    mask[[2, 7]] = 0
+    out = kl_logits(Z, idx, logit, mask, tau=tau)
+    tZ = torch.tensor(Z, requires_grad=True)
+    logq = torch.log_softmax(tZ / tau, dim=1)
+    p = torch.softmax(torch.tensor(logit) / tau, dim=1)
+    P = torch.zeros(T, V, dtype=torch.float64).scatter_add_(1, torch.tensor(idx.astype(np.int64)), p)
+    per_row = torch.nn.functional.kl_div(logq, P, reduction="none").sum(1)
+    m = torch.tensor(mask.astype(np.float64))
+    loss = (per_row * m).sum() / m.sum()
+    loss.backward()
+    assert abs(out["loss"] - loss.item()) < 1e-12
+    assert rel(out["dZ"], tZ.grad.numpy()) < 1e-11
+    assert np.all(out["dZ"][[2, 7]] == 0.0)
+
+
+def test_kl_logits_closed_forms_and_invariances():
+    """Z = 0 (uniform student): KL_t = sum_k p log p + log V and
+    dZ = (1/V - P)/(N tau); a per-row constant added to Z changes nothing;
+    every row of dZ sums to zero."""
+    T, V, K, tau = 6, 25, 4, 1.3
+    r = np.random.default_rng(3)
+    idx = np.stack([r.choice(V, K, replace=False) for _ in range(T)]).astype(np.int32)
+    logit = r.standard_normal((T, K))
+    out = kl_logits(np.zeros((T, V)), idx, logit, None, tau=tau)
+    u = logit / tau
+    p = np.exp(u - u.max(1, keepdims=True))
+    p /= p.sum(1, keepdims=True)
+    kl = np.sum(p * np.log(p), axis=1) + math.log(V)
+    assert np.max(np.abs(out["kl"] - kl)) < 1e-13
+    dz = np.full((T, V), 1.0 / V)
+    for t in range(T):
+        dz[t, idx[t]] -= p[t]
+    assert rel(out["dZ"], dz / (T * tau)) < 1e-13
+    Z = r.standard_normal((T, V)) * 2
+    a = kl_logits(Z, idx, logit, None, tau=tau)
+    b = kl_logits(Z + r.standard_normal((T, 1)) * 50, idx, logit, None, tau=tau)
+    assert abs(a["loss"] - b["loss"]) < 1e-11
+    assert rel(a["dZ"], b["dZ"]) < 1e-11
+    assert np.max(np.abs(a["dZ"].sum(1))) < 1e-15
+
+
+def test_kl_logits_finite_differences():
+    T, V, K, tau = 3, 12, 3, 1.7
+    r = np.random.default_rng(8)
+    Z = r.standard_normal((T, V))
+    idx = np.stack([r.choice(V, K, replace=False) for _ in range(T)]).astype(np.int32)
+    logit = r.standard_normal((T, K))
+    mask = np.array([1, 0, 1], np.uint8)
+    out = kl_logits(Z, idx, logit, mask, tau=tau)
+    eps = 1e-5
+    fd = np.zeros_like(Z)
+    for i in range(T):
+        for j in range(V):
+            zp = Z.copy(); zp[i, j] += eps
+            zm = Z.copy(); zm[i, j] -= eps
+            fd[i, j] = (kl_logits(zp, idx, logit, mask, tau, grads=False)["loss"]
+                        - kl_logits(zm, idx, logit, mask, tau, grads=False)["loss"]) / (2 * eps)
+    assert rel(out["dZ"], fd) < 1e-7
+
+
+# ------------------------------------------------------------ top-K selection
+def test_topk_rows_brute_force_with_ties():
+    """Against a pure-Python sort of (value, id) pairs, on rows full of ties."""
+    r = np.random.default_rng(9)
+    X = r.integers(-3, 4, size=(7, 23)).astype(np.float32)
+    X[2] = 1.0                      # a row of one value: ids 0..K-1
+    for K in (1, 5, 23):
+        idx, vals = topk_rows(X, K)
+        for t in range(X.shape[0]):
+            ref = sorted(range(X.shape[1]), key=lambda v: (-float(X[t, v]), v))[:K]
+            assert idx[t].tolist() == ref
+            assert vals[t].tolist() == [float(X[t, v]) for v in ref]
+    assert topk_rows(X, 4)[0][2].tolist() == [0, 1, 2, 3]
+
+
+def test_topk_rows_distinct_values_match_library_selection():
+    r = np.random.default_rng(10)
+    X = r.standard_normal((5, 1000))
+    idx, vals = topk_rows(X, 64)
+    for t in range(5):
+        top = np.argpartition(-X[t], 64)[:64]
+        assert set(top.tolist()) == set(idx[t].tolist())
+        assert np.all(np.diff(vals[t]) < 0)
