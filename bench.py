@@ -6,7 +6,8 @@ One step = one kd_topk_kl_fwd_bwd call (teacher prep, gather, pass 1
 log-sum-exp, loss, pass 2 recompute + logit gradient + dH/dW contractions)
 over one synthetic batch already resident in HBM.  Prints one JSON line;
 its "seq_chunk" object times the same call under the sequence-chunk
-schedule (stored block logits instead of the pass-2 recompute).
+schedule (stored block logits instead of the pass-2 recompute), and
+"logits_variant" the forward-chunked KL on the batch's materialised logits.
 
 Other modes (not the benchmark line):
   --copy-probe      a plain device copy of known size, to calibrate rocprofv3
@@ -140,6 +141,48 @@ def run_seq_chunk(args, wl, x):
     return res
 
 
+def run_logits_variant(args, wl, x):
+    """Forward-chunked KL on the materialised bf16 logits of the same batch
+    (Z = h W^T): loss + dZ.  HBM-bound: the algorithmic traffic is one read
+    and one write of Z, 4 bytes per logit (the kernel's second read of a row
+    mostly hits the last-level cache)."""
+    import torch
+    import chunked_kl_loss_02_amd as kd
+    T, V = wl.T, wl.V
+    Z = torch.nn.functional.linear(x["h"], x["W"])
+    dZ = torch.empty_like(Z)
+    loss = torch.empty((), dtype=torch.float32, device=Z.device)
+    ws = torch.empty(kd.logits_workspace_size(T, V, wl.K, wl.tau), dtype=torch.uint8, device=Z.device)
+
+    def step():
+        kd.kl_logits(Z, x["teacher_idx"], x["teacher_logit"], x["mask"], wl.tau, workspace=ws, out=(loss, dZ))
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    kd.timing_enable(True)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    kd.timing_enable(False)
+    pk = kd.timing_collect()
+    row_ms, row_n = pk["logits"]
+    bytes_step = 4.0 * T * V
+    res = {"value": T * args.steps / dt, "unit": "tokens/s", "ms_per_step": dt * 1e3 / args.steps,
+           "roofline": {"bound": "hbm", "kernel": "k_lrow (row log-sum-exp + dZ)",
+                        "achieved": bytes_step * row_n / (row_ms * 1e-3) / 1e9 if row_ms > 0 else 0.0,
+                        "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                        "frac": bytes_step * row_n / (row_ms * 1e-3) / 1e9 / PEAK_HBM_GBS if row_ms > 0 else 0.0,
+                        "bytes_per_launch": bytes_step, "avg_launch_ms": row_ms / max(row_n, 1)},
+           "per_kernel_ms_per_step": {k: v[0] / args.steps for k, v in pk.items() if v[1]},
+           "loss": loss.item()}
+    del Z, dZ, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def run_one(args, wl):
     import numpy as np
     import torch
@@ -234,6 +277,7 @@ def main():
     ap.add_argument("--workload", default="gptoss", choices=["gptoss", "long", "qwen", "tiny"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-seq-chunk", action="store_true", help="skip the sequence-chunk schedule line")
+    ap.add_argument("--no-variants", action="store_true", help="skip the logits / top-K variant lines")
     ap.add_argument("--cpu-rows", type=int, default=2048)
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--sweep", action="store_true")
@@ -259,6 +303,8 @@ def main():
     res["config"]["schedule"] = "recompute (pass 2 recomputes each vocabulary chunk)"
     if not args.no_seq_chunk:
         res["seq_chunk"] = run_seq_chunk(args, wl, x)
+    if not args.no_variants:
+        res["logits_variant"] = run_logits_variant(args, wl, x)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(x, wl.tau, args.cpu_rows)
     else:

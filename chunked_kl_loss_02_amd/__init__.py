@@ -11,7 +11,7 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["fwd_bwd", "fwd", "bwd", "topk_kl_loss", "TopKKLLoss", "workspace_size", "fwd_workspace_size",
+__all__ = ["fwd_bwd", "fwd", "bwd", "topk_kl_loss", "kl_logits", "logits_workspace_size", "KdLogitsProblem", "TopKKLLoss", "workspace_size", "fwd_workspace_size",
            "saved_size", "lse", "saved_lse", "KdProblem", "library_path", "lib", "timing_enable",
            "timing_collect", "KERNEL_CLASSES", "KD_FLAG_VALIDATE", "KD_FLAG_ACCUMULATE_DH",
            "KD_FLAG_ACCUMULATE_DW", "KD_FLAG_GRAD_BF16", "KD_FLAG_SEQ_CHUNK"]
@@ -24,8 +24,9 @@ KD_FLAG_ACCUMULATE_DH = 2
 KD_FLAG_ACCUMULATE_DW = 4
 KD_FLAG_GRAD_BF16 = 8
 KD_FLAG_SEQ_CHUNK = 16
-ABI_VERSION = 2
-KERNEL_CLASSES = ("teacher", "gather", "pass1", "lse", "loss", "pass2", "fixup", "bwd", "other")
+ABI_VERSION = 3
+KD_FLAG_LOGITS_F32 = 32
+KERNEL_CLASSES = ("teacher", "gather", "pass1", "lse", "loss", "pass2", "fixup", "bwd", "other", "logits", "topk")
 _STATUS = {0: "KD_OK", 1: "KD_ERR_ARG", 2: "KD_ERR_UNSUPPORTED", 3: "KD_ERR_WORKSPACE",
            4: "KD_ERR_INDEX", 5: "KD_ERR_NONFINITE", 6: "KD_ERR_HIP"}
 
@@ -34,6 +35,11 @@ class KdProblem(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int64), ("H", ctypes.c_int64), ("V", ctypes.c_int64),
                 ("K", ctypes.c_int32), ("tau", ctypes.c_float), ("chunk_v", ctypes.c_int32),
                 ("block_t", ctypes.c_int32), ("flags", ctypes.c_uint32)]
+
+
+class KdLogitsProblem(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int64), ("V", ctypes.c_int64), ("K", ctypes.c_int32), ("tau", ctypes.c_float),
+                ("flags", ctypes.c_uint32)]
 
 
 class KdError(RuntimeError):
@@ -77,6 +83,11 @@ def lib():
     L.kd_timing_enable.restype = ctypes.c_int
     L.kd_timing_collect.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
     L.kd_timing_collect.restype = ctypes.c_int
+    LP = ctypes.POINTER(KdLogitsProblem)
+    L.kd_topk_kl_logits_workspace_size.argtypes = [LP, ctypes.POINTER(sz)]
+    L.kd_topk_kl_logits_workspace_size.restype = ctypes.c_int
+    L.kd_topk_kl_logits.argtypes = [LP, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.kd_topk_kl_logits.restype = ctypes.c_int
     if L.kd_abi_version() != ABI_VERSION:
         raise RuntimeError(f"{library_path} has ABI {L.kd_abi_version()}, this binding expects {ABI_VERSION}: rebuild it")
     _lib = L
@@ -335,7 +346,61 @@ def timing_enable(on=True):
 
 def timing_collect():
     """{class: (total_ms, launches)} for the launches recorded since enabling."""
-    ms = (ctypes.c_double * 9)()
-    cnt = (ctypes.c_int64 * 9)()
+    n = len(KERNEL_CLASSES)
+    ms = (ctypes.c_double * n)()
+    cnt = (ctypes.c_int64 * n)()
     _raise(lib().kd_timing_collect(ms, cnt))
-    return {KERNEL_CLASSES[i]: (ms[i], cnt[i]) for i in range(9)}
+    return {KERNEL_CLASSES[i]: (ms[i], cnt[i]) for i in range(n)}
+
+
+def logits_workspace_size(T, V, K, tau=1.0, f32=False) -> int:
+    p = KdLogitsProblem(int(T), int(V), int(K), float(tau), KD_FLAG_LOGITS_F32 if f32 else 0)
+    n = ctypes.c_size_t(0)
+    _raise(lib().kd_topk_kl_logits_workspace_size(ctypes.byref(p), ctypes.byref(n)))
+    return n.value
+
+
+def kl_logits(Z, teacher_idx, teacher_logit, mask=None, tau=1.0, *, grad=True, row_loss=False, validate=False,
+              workspace=None, out=None):
+    """Forward-chunked KL on materialised student logits Z [T,V] (bf16 or
+    fp32): (loss, dZ[, row_loss]); dZ has Z's dtype (None with grad=False).
+    `out` may pass preallocated (loss, dZ[, row_loss])."""
+    import torch
+    if Z.dim() != 2 or Z.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("Z must be a 2-D bfloat16 or float32 tensor")
+    T, V = Z.shape
+    K = teacher_idx.shape[1] if teacher_idx.dim() == 2 else 0
+    dev = Z.device
+    if dev.type != "cuda" or not Z.is_contiguous():
+        raise ValueError("Z must be a contiguous GPU tensor")
+    if teacher_idx.dtype != torch.int32 or teacher_logit.dtype != torch.float32:
+        raise TypeError("teacher_idx must be int32 and teacher_logit float32")
+    for name, t in (("teacher_idx", teacher_idx), ("teacher_logit", teacher_logit)):
+        if not t.is_contiguous() or t.device != dev or tuple(t.shape) != (T, K):
+            raise ValueError(f"{name} must be a contiguous [T, K] tensor on {dev}")
+    if mask is not None:
+        if mask.dtype == torch.bool:
+            mask = mask.view(torch.uint8)
+        if mask.dtype != torch.uint8 or mask.shape != (T,) or not mask.is_contiguous() or mask.device != dev:
+            raise ValueError("mask must be a contiguous uint8/bool [T] tensor on the same device")
+    f32 = Z.dtype == torch.float32
+    p = KdLogitsProblem(int(T), int(V), int(K), float(tau),
+                        (KD_FLAG_LOGITS_F32 if f32 else 0) | (KD_FLAG_VALIDATE if validate else 0))
+    n = ctypes.c_size_t(0)
+    _raise(lib().kd_topk_kl_logits_workspace_size(ctypes.byref(p), ctypes.byref(n)))
+    workspace = _workspace(workspace, n.value, dev)
+    if out is not None:
+        loss, dZ = out[0], out[1]
+        rl = out[2] if row_loss else None
+        _check_out(loss, (), torch.float32, dev, "loss")
+        _check_out(dZ, (T, V), Z.dtype, dev, "dZ")
+        _check_out(rl, (T,), torch.float32, dev, "row_loss")
+    else:
+        loss = torch.empty((), dtype=torch.float32, device=dev)
+        dZ = torch.empty((T, V), dtype=Z.dtype, device=dev) if grad else None
+        rl = torch.empty((T,), dtype=torch.float32, device=dev) if row_loss else None
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    _raise(lib().kd_topk_kl_logits(ctypes.byref(p), _ptr(Z), _ptr(teacher_idx), _ptr(teacher_logit), _ptr(mask),
+                                   _ptr(loss), _ptr(dZ), _ptr(rl), _ptr(workspace),
+                                   ctypes.c_size_t(workspace.numel()), ctypes.c_void_p(stream)))
+    return (loss, dZ, rl) if row_loss else (loss, dZ)

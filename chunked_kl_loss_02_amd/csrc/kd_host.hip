@@ -9,6 +9,7 @@
 
 #include "../../include/kdkl.h"
 #include "kd_kernels.hpp"
+#include "kd_logits.hpp"
 
 namespace {
 
@@ -131,6 +132,7 @@ struct TimedLaunch {
   hipEvent_t a, b;
 };
 bool g_timing = false;
+constexpr int kTimingClasses = 11;
 std::vector<TimedLaunch> g_launches;
 std::vector<hipEvent_t> g_pool;
 
@@ -526,7 +528,7 @@ kd_status finish(Launcher& L, bool validate, const uint32_t* status) {
 
 extern "C" {
 
-int kd_abi_version(void) { return 2; }
+int kd_abi_version(void) { return 3; }
 
 const char* kd_status_string(kd_status s) {
   switch (s) {
@@ -566,7 +568,7 @@ kd_status kd_timing_collect(double* ms, int64_t* launches) {
     if (hipEventSynchronize(l.b) != hipSuccess) st = KD_ERR_HIP;
     float t = 0.f;
     if (hipEventElapsedTime(&t, l.a, l.b) != hipSuccess) st = KD_ERR_HIP;
-    if (l.cls >= 0 && l.cls < 9) {
+    if (l.cls >= 0 && l.cls < kTimingClasses) {
       if (ms) ms[l.cls] += t;
       if (launches) launches[l.cls] += 1;
     }
@@ -672,6 +674,155 @@ kd_status kd_topk_kl_bwd(const kd_problem* p, const uint16_t* h, const uint16_t*
   launch_prep(L, P, in, b, validate, grad_loss);
   launch_backward(L, P, p->flags, in, b, dH, dW);
   return finish(L, validate, b.status);
+}
+
+}  // extern "C"
+
+// ------------------------------------------------ KL on given student logits
+namespace {
+
+struct LogitsPlan {
+  int64_t T, V, Tp;
+  int K;
+  size_t o_p, o_pm, o_s, o_neg, o_lse2, o_row, o_bsum, o_scal_f, o_scal_i, o_status, total;
+};
+
+kd_status check_logits(const kd_logits_problem* p) {
+  if (!p) return KD_ERR_ARG;
+  if (p->T < 0 || p->V <= 0 || p->K <= 0 || (int64_t)p->K > p->V) return KD_ERR_ARG;
+  if (!(p->tau > 0.f) || !isfinite(p->tau)) return KD_ERR_ARG;
+  if (p->flags & ~(KD_FLAG_VALIDATE | KD_FLAG_LOGITS_F32)) return KD_ERR_ARG;
+  if (p->K > kd::kTeacherMaxK) return KD_ERR_UNSUPPORTED;
+  if (p->V > (int64_t)INT32_MAX || p->T > ((int64_t)1 << 40) || p->T > (int64_t)INT32_MAX) return KD_ERR_UNSUPPORTED;
+  return KD_OK;
+}
+
+LogitsPlan logits_plan(const kd_logits_problem* p) {
+  LogitsPlan P{};
+  P.T = p->T;
+  P.V = p->V;
+  P.K = p->K;
+  P.Tp = align256(std::max<int64_t>(P.T, 1));
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t r = o; o += (bytes + 255) & ~size_t(255); return r; };
+  P.o_p = take((size_t)P.T * P.K * 4);
+  P.o_pm = take((size_t)P.T * P.K * 4);
+  P.o_s = take((size_t)P.T * P.K * 4);
+  P.o_neg = take((size_t)P.Tp * 4);
+  P.o_lse2 = take((size_t)P.Tp * 4);
+  P.o_row = take((size_t)P.Tp * 4);
+  P.o_bsum = take((size_t)cdiv(P.Tp, 256) * 8 + 8);
+  P.o_scal_f = take(64);
+  P.o_scal_i = take(64);
+  P.o_status = take(64);
+  P.total = o;
+  return P;
+}
+
+}  // namespace
+
+extern "C" {
+
+kd_status kd_topk_kl_logits_workspace_size(const kd_logits_problem* p, size_t* bytes) {
+  if (!bytes) return KD_ERR_ARG;
+  const kd_status st = check_logits(p);
+  if (st != KD_OK) return st;
+  *bytes = logits_plan(p).total;
+  return KD_OK;
+}
+
+kd_status kd_topk_kl_logits(const kd_logits_problem* p, const void* Z, const int32_t* teacher_idx,
+                            const float* teacher_logit, const uint8_t* mask, float* loss, void* dZ,
+                            float* row_loss, void* workspace, size_t workspace_bytes, void* stream) {
+  const kd_status st = check_logits(p);
+  if (st != KD_OK) return st;
+  if (!loss || !workspace) return KD_ERR_ARG;
+  if (p->T > 0 && (!Z || !teacher_idx || !teacher_logit)) return KD_ERR_ARG;
+  if (misaligned(Z, 16) || misaligned(dZ, 16) || misaligned(workspace, 256) || misaligned(teacher_idx, 4) ||
+      misaligned(teacher_logit, 4) || misaligned(loss, 4) || misaligned(row_loss, 4))
+    return KD_ERR_UNSUPPORTED;
+  const LogitsPlan P = logits_plan(p);
+  if (workspace_bytes < P.total) return KD_ERR_WORKSPACE;
+  Launcher L{static_cast<hipStream_t>(stream)};
+  hipStream_t s = L.s;
+  char* ws = static_cast<char*>(workspace);
+  float* tp = reinterpret_cast<float*>(ws + P.o_p);
+  float* tpm = reinterpret_cast<float*>(ws + P.o_pm);
+  float* ts = reinterpret_cast<float*>(ws + P.o_s);
+  float* neg = reinterpret_cast<float*>(ws + P.o_neg);
+  float* lse2 = reinterpret_cast<float*>(ws + P.o_lse2);
+  float* rows_out = row_loss ? row_loss : reinterpret_cast<float*>(ws + P.o_row);
+  double* bsum = reinterpret_cast<double*>(ws + P.o_bsum);
+  float* scal_f = reinterpret_cast<float*>(ws + P.o_scal_f);
+  int64_t* scal_i = reinterpret_cast<int64_t*>(ws + P.o_scal_i);
+  uint32_t* status = reinterpret_cast<uint32_t*>(ws + P.o_status);
+  const bool validate = (p->flags & KD_FLAG_VALIDATE) != 0;
+  const bool f32 = (p->flags & KD_FLAG_LOGITS_F32) != 0;
+  const int64_t T = P.T, V = P.V;
+  const int K = P.K;
+  using namespace kd;
+  if (T == 0) {
+    L.run(8, [&] { k_fill<<<1, 64, 0, s>>>(loss, 1, 0.f); });
+    return finish(L, false, nullptr);
+  }
+  if (validate) L.run(8, [&] { k_fill<<<1, 64, 0, s>>>(reinterpret_cast<float*>(status), 1, 0.f); });
+  L.run(4, [&] { k_count<<<1, 1024, 0, s>>>(mask, T, p->tau, nullptr, scal_f, scal_i); });
+  L.run(0, [&] {
+    k_teacher<<<(unsigned)cdiv(T, 4), 256, 0, s>>>(teacher_idx, teacher_logit, mask, T, K, V, 1.0f / p->tau, tp, tpm,
+                                                    neg, status, validate ? 1 : 0);
+  });
+  LrowArgs a{};
+  a.Z = Z;
+  a.dZ = dZ;
+  a.T = T;
+  a.V = V;
+  a.K = K;
+  a.idx = teacher_idx;
+  a.pm = tpm;
+  a.mask = mask;
+  a.scal_f = scal_f;
+  a.lse2 = lse2;
+  a.s_out = ts;
+  a.c = kLog2e / p->tau;
+  const bool vec = (V * (f32 ? 4 : 2)) % 16 == 0;
+  // bf16 rows that fit 512 threads x PER 16-byte chunks stay in registers
+  const int64_t need = cdiv(V / 8, kLrowRegThreads);
+  static const int kPer[] = {1, 2, 4, 8, 16, 24, 32, 40, 50};
+  int per = 0;
+  if (!f32 && vec)
+    for (int c : kPer)
+      if (c >= need) {
+        per = c;
+        break;
+      }
+  L.run(9, [&] {
+    if (per) {
+      const unsigned g = (unsigned)T;
+      switch (per) {
+        case 1: k_lrow_reg<1><<<g, kLrowRegThreads, 0, s>>>(a); break;
+        case 2: k_lrow_reg<2><<<g, kLrowRegThreads, 0, s>>>(a); break;
+        case 4: k_lrow_reg<4><<<g, kLrowRegThreads, 0, s>>>(a); break;
+        case 8: k_lrow_reg<8><<<g, kLrowRegThreads, 0, s>>>(a); break;
+        case 16: k_lrow_reg<16><<<g, kLrowRegThreads, 0, s>>>(a); break;
+        case 24: k_lrow_reg<24><<<g, kLrowRegThreads, 0, s>>>(a); break;
+        case 32: k_lrow_reg<32><<<g, kLrowRegThreads, 0, s>>>(a); break;
+        case 40: k_lrow_reg<40><<<g, kLrowRegThreads, 0, s>>>(a); break;
+        default: k_lrow_reg<50><<<g, kLrowRegThreads, 0, s>>>(a); break;
+      }
+    } else if (f32) {
+      if (vec) k_lrow<float, true><<<(unsigned)T, kLrowThreads, 0, s>>>(a);
+      else k_lrow<float, false><<<(unsigned)T, kLrowThreads, 0, s>>>(a);
+    } else {
+      if (vec) k_lrow<uint16_t, true><<<(unsigned)T, kLrowThreads, 0, s>>>(a);
+      else k_lrow<uint16_t, false><<<(unsigned)T, kLrowThreads, 0, s>>>(a);
+    }
+  });
+  const int64_t nb = cdiv(T, 256);
+  L.run(4, [&] {
+    k_rows<<<(unsigned)nb, 256, 0, s>>>(tp, ts, neg, lse2, mask, T, K, 1.0f / p->tau, rows_out, bsum);
+  });
+  L.run(4, [&] { k_sum<<<1, 1024, 0, s>>>(bsum, nb, scal_f, loss); });
+  return finish(L, validate, status);
 }
 
 }  // extern "C"

@@ -152,6 +152,39 @@ kd_status kd_topk_kl_bwd(const kd_problem* p,
                          void* dH, void* dW,
                          void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Forward-chunked KL on materialised student logits.  The page "Making
+ * Knowledge Distillation Cheap Enough to Run at Scale", section "Two systems
+ * changes", describes this variant: the teacher stays sparse (its cached
+ * top-K) while the student's logits Z[T,V] exist in full; the loss is the
+ * same, and the gradient returned is the one with respect to the logits:
+ *
+ *   dZ[t,v] = mask_t (softmax_v(Z[t,:]/tau) - P[t,v]) / (N tau)
+ *
+ * It reads Z once for the log-sum-exp and once more for dZ (HBM-bound).
+ */
+#define KD_FLAG_LOGITS_F32 32u  /* Z and dZ are fp32 (default: bf16 bit patterns) */
+
+typedef struct kd_logits_problem {
+  int64_t T;        /* rows of Z; 0 allowed (loss = 0) */
+  int64_t V;        /* vocabulary size; >= 1 */
+  int32_t K;        /* cached teacher entries per row; 1 <= K <= min(V, 1024) */
+  float tau;        /* temperature; finite, > 0 */
+  uint32_t flags;   /* KD_FLAG_VALIDATE | KD_FLAG_LOGITS_F32 */
+} kd_logits_problem;
+
+kd_status kd_topk_kl_logits_workspace_size(const kd_logits_problem* p, size_t* bytes);
+
+/*   Z             [T,V]  bf16 (or fp32) student logits, row-major, device, 16-byte aligned
+ *   teacher_idx, teacher_logit, mask, loss, row_loss: as kd_topk_kl_fwd_bwd
+ *   dZ            [T,V]  same type as Z, device, 16-byte aligned, overwritten; NULL = loss only
+ * Rows whose byte length is not a multiple of 16 take a slower element-wise
+ * path.  Same conventions (errors, ownership, asynchrony) as above. */
+kd_status kd_topk_kl_logits(const kd_logits_problem* p, const void* Z,
+                            const int32_t* teacher_idx, const float* teacher_logit,
+                            const uint8_t* mask, float* loss, void* dZ, float* row_loss,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
 /* Device address, inside a workspace used by the last completed call with
  * problem p, of the per-token log-sum-exp of S/tau (natural log would be
  * value * ln 2: the array holds log2 of sum_v 2^(log2(e) S[t,v]/tau), fp32,
@@ -162,16 +195,18 @@ const float* kd_topk_kl_workspace_lse2(const kd_problem* p, const void* workspac
 const char* kd_status_string(kd_status s);
 
 /* ABI version (incremented on any change of the declarations above; 2 adds
- * the split forward / backward entry points and the gradient flags). */
+ * the split forward / backward entry points and the gradient flags, 3 the
+ * logits variant, the top-K selection and two more timing classes). */
 int kd_abi_version(void);
 
 /* Optional per-kernel timing with HIP events recorded on the launch stream
  * around every launch of the library's kernels while enabled.  Intended for
  * benchmarks; not thread-safe.  Kernel classes: 0 teacher, 1 gather,
- * 2 pass1, 3 lse, 4 loss, 5 pass2, 6 fixup, 7 bwd, 8 other.
+ * 2 pass1, 3 lse, 4 loss, 5 pass2, 6 fixup, 7 bwd, 8 other, 9 logits (the
+ * row kernel of kd_topk_kl_logits), 10 topk (kd_topk_select).
  * kd_timing_collect synchronises the recorded events, adds each class's
- * elapsed milliseconds and launch count to ms[9] / launches[9] (either may be
- * NULL) and releases the events. */
+ * elapsed milliseconds and launch count to ms[11] / launches[11] (either may
+ * be NULL) and releases the events. */
 kd_status kd_timing_enable(int on);
 kd_status kd_timing_collect(double* ms, int64_t* launches);
 
