@@ -178,7 +178,28 @@ def run_logits_variant(args, wl, x):
                         "bytes_per_launch": bytes_step, "avg_launch_ms": row_ms / max(row_n, 1)},
            "per_kernel_ms_per_step": {k: v[0] / args.steps for k, v in pk.items() if v[1]},
            "loss": loss.item()}
-    del Z, dZ, ws
+    # the teacher-cache producer on the same [T, V] bf16 grid: top-K per row
+    idx = torch.empty((T, wl.K), dtype=torch.int32, device=Z.device)
+    val = torch.empty((T, wl.K), dtype=torch.float32, device=Z.device)
+    for _ in range(args.warmup):
+        kd.topk_select(Z, wl.K, out=(idx, val))
+    torch.cuda.synchronize()
+    kd.timing_enable(True)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        kd.topk_select(Z, wl.K, out=(idx, val))
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    kd.timing_enable(False)
+    tk_ms, tk_n = kd.timing_collect()["topk"]
+    tk_bytes = 2.0 * T * V + 8.0 * T * wl.K
+    res["topk_variant"] = {
+        "value": T * args.steps / dt, "unit": "rows/s", "ms_per_step": dt * 1e3 / args.steps, "K": wl.K,
+        "roofline": {"bound": "hbm", "kernel": "k_topk (per-row top-K of bf16 logits)",
+                     "achieved": tk_bytes * tk_n / (tk_ms * 1e-3) / 1e9 if tk_ms > 0 else 0.0, "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": tk_bytes * tk_n / (tk_ms * 1e-3) / 1e9 / PEAK_HBM_GBS if tk_ms > 0 else 0.0,
+                     "bytes_per_launch": tk_bytes, "avg_launch_ms": tk_ms / max(tk_n, 1)}}
+    del Z, dZ, ws, idx, val
     torch.cuda.empty_cache()
     return res
 

@@ -11,7 +11,8 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["fwd_bwd", "fwd", "bwd", "topk_kl_loss", "kl_logits", "logits_workspace_size", "KdLogitsProblem", "TopKKLLoss", "workspace_size", "fwd_workspace_size",
+__all__ = ["fwd_bwd", "fwd", "bwd", "topk_kl_loss", "kl_logits", "logits_workspace_size", "KdLogitsProblem",
+           "topk_select", "KdTopkProblem", "TopKKLLoss", "workspace_size", "fwd_workspace_size",
            "saved_size", "lse", "saved_lse", "KdProblem", "library_path", "lib", "timing_enable",
            "timing_collect", "KERNEL_CLASSES", "KD_FLAG_VALIDATE", "KD_FLAG_ACCUMULATE_DH",
            "KD_FLAG_ACCUMULATE_DW", "KD_FLAG_GRAD_BF16", "KD_FLAG_SEQ_CHUNK"]
@@ -40,6 +41,10 @@ class KdProblem(ctypes.Structure):
 class KdLogitsProblem(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int64), ("V", ctypes.c_int64), ("K", ctypes.c_int32), ("tau", ctypes.c_float),
                 ("flags", ctypes.c_uint32)]
+
+
+class KdTopkProblem(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int64), ("V", ctypes.c_int64), ("K", ctypes.c_int32), ("flags", ctypes.c_uint32)]
 
 
 class KdError(RuntimeError):
@@ -88,6 +93,8 @@ def lib():
     L.kd_topk_kl_logits_workspace_size.restype = ctypes.c_int
     L.kd_topk_kl_logits.argtypes = [LP, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.kd_topk_kl_logits.restype = ctypes.c_int
+    L.kd_topk_select.argtypes = [ctypes.POINTER(KdTopkProblem), vp, vp, vp, vp]
+    L.kd_topk_select.restype = ctypes.c_int
     if L.kd_abi_version() != ABI_VERSION:
         raise RuntimeError(f"{library_path} has ABI {L.kd_abi_version()}, this binding expects {ABI_VERSION}: rebuild it")
     _lib = L
@@ -404,3 +411,25 @@ def kl_logits(Z, teacher_idx, teacher_logit, mask=None, tau=1.0, *, grad=True, r
                                    _ptr(loss), _ptr(dZ), _ptr(rl), _ptr(workspace),
                                    ctypes.c_size_t(workspace.numel()), ctypes.c_void_p(stream)))
     return (loss, dZ, rl) if row_loss else (loss, dZ)
+
+
+def topk_select(X, K, *, out=None):
+    """The K largest values of every row of X [T,V] (bf16, on the GPU): ids
+    (int32 [T,K], descending value, equal values by ascending id) and values
+    (fp32 [T,K]) -- the content of the teacher's top-K cache."""
+    import torch
+    if X.dim() != 2 or X.dtype != torch.bfloat16 or X.device.type != "cuda" or not X.is_contiguous():
+        raise TypeError("X must be a contiguous 2-D bfloat16 GPU tensor")
+    T, V = X.shape
+    dev = X.device
+    if out is not None:
+        idx, val = out
+        _check_out(idx, (T, K), torch.int32, dev, "idx")
+        _check_out(val, (T, K), torch.float32, dev, "values")
+    else:
+        idx = torch.empty((T, K), dtype=torch.int32, device=dev)
+        val = torch.empty((T, K), dtype=torch.float32, device=dev)
+    p = KdTopkProblem(int(T), int(V), int(K), 0)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    _raise(lib().kd_topk_select(ctypes.byref(p), _ptr(X), _ptr(idx), _ptr(val), ctypes.c_void_p(stream)))
+    return idx, val

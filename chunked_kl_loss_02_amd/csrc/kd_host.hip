@@ -10,6 +10,7 @@
 #include "../../include/kdkl.h"
 #include "kd_kernels.hpp"
 #include "kd_logits.hpp"
+#include "kd_topk.hpp"
 
 namespace {
 
@@ -823,6 +824,31 @@ kd_status kd_topk_kl_logits(const kd_logits_problem* p, const void* Z, const int
   });
   L.run(4, [&] { k_sum<<<1, 1024, 0, s>>>(bsum, nb, scal_f, loss); });
   return finish(L, validate, status);
+}
+
+kd_status kd_topk_select(const kd_topk_problem* p, const uint16_t* X, int32_t* idx, float* values,
+                         void* stream) {
+  if (!p) return KD_ERR_ARG;
+  if (p->T < 0 || p->V <= 0 || p->K <= 0 || (int64_t)p->K > p->V || p->flags != 0) return KD_ERR_ARG;
+  if (p->T > 0 && (!X || !idx || !values)) return KD_ERR_ARG;
+  using namespace kd;
+  if (p->K > kTopkMaxK || p->V % 8 != 0 || p->V > (int64_t)INT32_MAX / 2 || p->T > (int64_t)INT32_MAX)
+    return KD_ERR_UNSUPPORTED;
+  if (misaligned(X, 16) || misaligned(idx, 4) || misaligned(values, 4)) return KD_ERR_UNSUPPORTED;
+  Launcher L{static_cast<hipStream_t>(stream)};
+  if (p->T == 0) return finish(L, false, nullptr);
+  hipStream_t s = L.s;
+  TopkArgs a{};
+  a.X = X;
+  a.idx = idx;
+  a.val = values;
+  a.V = p->V;
+  a.K = p->K;
+  int bits = 0;
+  while (((int64_t)1 << bits) < p->V) ++bits;
+  a.id_bits = bits;
+  L.run(10, [&] { k_topk<<<(unsigned)p->T, kTopkThreads, 0, s>>>(a); });
+  return finish(L, false, nullptr);
 }
 
 }  // extern "C"

@@ -1,0 +1,218 @@
+// Top-K selection per row: the producer of the teacher cache (the page
+// "Making Knowledge Distillation Cheap Enough to Run at Scale", section "Two
+// systems changes": the K most likely tokens per position are computed once
+// and cached).  For every row of X[T,V] (bf16): the ids of its K largest
+// values in descending order, equal values by ascending id, and the values.
+//
+// One 512-thread workgroup per row, values compared as 16-bit
+// order-preserving keys:
+//   1. one pass over the row keeps each thread's two largest keys; the K-th
+//      largest of those 1024 keys, theta, is a lower bound of the row's K-th
+//      largest (K distinct elements reach it), found bit by bit;
+//   2. a second pass appends every (key, id) with key >= theta to LDS (for
+//      ordinary rows a small multiple of K; the second read mostly hits the
+//      last-level cache);
+//   3. the candidates are sorted in LDS (bitonic: descending key, ascending
+//      id) and the first K written out.
+// Rows where more than kTopkCand keys reach theta (e.g. long runs of equal
+// values) take an exact slow path: the K-th largest key and the cut among
+// its ties are found bit by bit with a pass over the row per bit, then
+// exactly K entries are collected.
+#pragma once
+#include "kd_common.hpp"
+
+namespace kd {
+
+constexpr int kTopkThreads = 512;
+constexpr int kTopkMaxK = 1024;
+constexpr int kTopkCand = 4096;
+
+// order-preserving 16-bit key of a bf16 bit pattern (-0 taken as +0)
+__device__ __forceinline__ uint32_t bf16_key(uint32_t b) {
+  b = (b == 0x8000u) ? 0u : b;
+  return (b & 0x8000u) ? (~b & 0xFFFFu) : (b | 0x8000u);
+}
+__device__ __forceinline__ float key_bf16_value(uint32_t k) {
+  const uint32_t b = (k & 0x8000u) ? (k & 0x7FFFu) : (~k & 0xFFFFu);
+  return __uint_as_float(b << 16);
+}
+
+struct TopkArgs {
+  const uint16_t* X;  // [T, V] bf16, V % 8 == 0
+  int32_t* idx;       // [T, K]
+  float* val;         // [T, K]
+  int64_t V;
+  int K;
+  int id_bits;        // bits of the largest id (V - 1)
+};
+
+// workgroup-wide sum of one int per thread; red: kTopkThreads / 64 ints of
+// LDS, alternated by the caller between consecutive calls so that one
+// barrier per call suffices
+__device__ __forceinline__ int block_count(int v, int* red) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  int s = 0;
+#pragma unroll
+  for (int q = 0; q < kTopkThreads / 64; ++q) s += red[q];
+  return s;
+}
+
+// the 8 keys of vector i of the row
+__device__ __forceinline__ void load_keys(const uint16_t* row, int64_t i, uint32_t (&k)[8]) {
+  const u32x4 v = reinterpret_cast<const u32x4*>(row)[i];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    k[2 * q] = bf16_key(v[q] & 0xFFFFu);
+    k[2 * q + 1] = bf16_key(v[q] >> 16);
+  }
+}
+
+// Sorts n entries (n a power of two, <= capacity) of (key, id) in LDS:
+// larger key first, then smaller id.
+__device__ __forceinline__ void lds_sort(uint32_t* key, int32_t* id, int n) {
+  for (int size = 2; size <= n; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int i = threadIdx.x; i < n; i += kTopkThreads) {
+        const int j = i ^ stride;
+        if (j > i) {
+          const uint32_t ki = key[i], kj = key[j];
+          const int32_t ii = id[i], ij = id[j];
+          const bool j_first = kj > ki || (kj == ki && ij < ii);
+          if ((i & size) == 0 ? j_first : !j_first) {
+            key[i] = kj;
+            key[j] = ki;
+            id[i] = ij;
+            id[j] = ii;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+__global__ void __launch_bounds__(kTopkThreads) k_topk(TopkArgs a) {
+  __shared__ uint32_t ck[kTopkCand];
+  __shared__ int32_t ci[kTopkCand];
+  __shared__ int red[2][kTopkThreads / 64];
+  __shared__ int ncand;
+  const int tid = threadIdx.x;
+  const int64_t t = blockIdx.x;
+  const int64_t V = a.V, nvec = V >> 3;
+  const int K = a.K;
+  const uint16_t* row = a.X + t * V;
+  int rb = 0;
+  // 1. each thread's two largest keys; theta = K-th largest of them
+  uint32_t m1 = 0, m2 = 0;
+  for (int64_t i = tid; i < nvec; i += kTopkThreads) {
+    uint32_t k[8];
+    load_keys(row, i, k);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const uint32_t lo = k[q] < m1 ? k[q] : m1;
+      m1 = k[q] > m1 ? k[q] : m1;
+      m2 = lo > m2 ? lo : m2;
+    }
+  }
+  if (tid == 0) ncand = 0;
+  uint32_t theta = 0;
+  for (int b = 15; b >= 0; --b) {
+    const uint32_t cand = theta | (1u << b);
+    if (block_count((m1 >= cand) + (m2 >= cand), red[rb]) >= K) theta = cand;
+    rb ^= 1;
+  }
+  // the elements behind the 1024 kept keys are distinct, so at least K keys
+  // of the row are >= theta
+  // 2. candidates: every key >= theta
+  for (int64_t i = tid; i < nvec; i += kTopkThreads) {
+    uint32_t k[8];
+    load_keys(row, i, k);
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      if (k[q] >= theta) {
+        const int p = atomicAdd(&ncand, 1);
+        if (p < kTopkCand) {
+          ck[p] = k[q];
+          ci[p] = (int32_t)(8 * i + q);
+        }
+      }
+  }
+  __syncthreads();
+  const int nc = ncand;
+  int ns;  // entries to sort
+  if (nc <= kTopkCand) {
+    ns = nc;
+  } else {
+    // exact slow path: x = K-th largest key; r of its ties, the smallest ids
+    uint32_t x = 0;
+    for (int b = 15; b >= 0; --b) {
+      const uint32_t cand = x | (1u << b);
+      int n = 0;
+      for (int64_t i = tid; i < nvec; i += kTopkThreads) {
+        uint32_t k[8];
+        load_keys(row, i, k);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) n += k[q] >= cand;
+      }
+      if (block_count(n, red[rb]) >= K) x = cand;
+      rb ^= 1;
+    }
+    int ngt = 0;
+    for (int64_t i = tid; i < nvec; i += kTopkThreads) {
+      uint32_t k[8];
+      load_keys(row, i, k);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) ngt += k[q] > x;
+    }
+    const int r = K - block_count(ngt, red[rb]);
+    rb ^= 1;
+    // largest y with #{key == x, id < y} < r; the ties with id <= y are taken
+    uint32_t y = 0;
+    for (int b = a.id_bits - 1; b >= 0; --b) {
+      const uint32_t cand = y | (1u << b);
+      int n = 0;
+      for (int64_t i = tid; i < nvec; i += kTopkThreads) {
+        uint32_t k[8];
+        load_keys(row, i, k);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) n += k[q] == x && (uint32_t)(8 * i + q) < cand;
+      }
+      if (block_count(n, red[rb]) < r) y = cand;
+      rb ^= 1;
+    }
+    if (tid == 0) ncand = 0;
+    __syncthreads();
+    for (int64_t i = tid; i < nvec; i += kTopkThreads) {
+      uint32_t k[8];
+      load_keys(row, i, k);
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        if (k[q] > x || (k[q] == x && (uint32_t)(8 * i + q) <= y)) {
+          const int p = atomicAdd(&ncand, 1);
+          if (p < kTopkCand) {
+            ck[p] = k[q];
+            ci[p] = (int32_t)(8 * i + q);
+          }
+        }
+    }
+    __syncthreads();
+    ns = K;
+  }
+  int np = 1;
+  while (np < ns) np <<= 1;
+  for (int i = ns + tid; i < np; i += kTopkThreads) {
+    ck[i] = 0u;
+    ci[i] = INT32_MAX;
+  }
+  __syncthreads();
+  lds_sort(ck, ci, np);
+  for (int k = tid; k < K; k += kTopkThreads) {
+    a.idx[t * K + k] = ci[k];
+    a.val[t * K + k] = key_bf16_value(ck[k]);
+  }
+}
+
+}  // namespace kd

@@ -185,6 +185,28 @@ kd_status kd_topk_kl_logits(const kd_logits_problem* p, const void* Z,
                             const uint8_t* mask, float* loss, void* dZ, float* row_loss,
                             void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Top-K selection: the producer of the teacher cache (the page "Making
+ * Knowledge Distillation Cheap Enough to Run at Scale", section "Two systems
+ * changes": the teacher's K most likely tokens per position are computed
+ * once and cached).  For every row of X[T,V] (teacher logits, bf16 bit
+ * patterns, row-major, device, 16-byte aligned) it writes the ids of the K
+ * largest values in descending order of value, equal values by ascending id
+ * (so the result is unique; -0 counts as +0), and the values (exact, fp32).
+ * Values are ordered as real numbers; NaN rows are a precondition violation.
+ * v1 limits: V % 8 == 0 (KD_ERR_UNSUPPORTED otherwise), 1 <= K <= min(V, 1024).
+ * No workspace; asynchronous on `stream`.
+ */
+typedef struct kd_topk_problem {
+  int64_t T;        /* rows; 0 allowed */
+  int64_t V;        /* row length */
+  int32_t K;        /* entries per row */
+  uint32_t flags;   /* must be 0 */
+} kd_topk_problem;
+
+kd_status kd_topk_select(const kd_topk_problem* p, const uint16_t* X,
+                         int32_t* idx, float* values, void* stream);
+
 /* Device address, inside a workspace used by the last completed call with
  * problem p, of the per-token log-sum-exp of S/tau (natural log would be
  * value * ln 2: the array holds log2 of sum_v 2^(log2(e) S[t,v]/tau), fp32,
