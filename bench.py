@@ -32,7 +32,8 @@ PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "bwd_traffic_gptoss.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "chunked_kl_loss_02_amd", "csrc", f)
-                  for f in ("kd_common.hpp", "kd_gemm.hpp", "kd_kernels.hpp", "kd_host.hip")]
+                  for f in ("kd_common.hpp", "kd_gemm.hpp", "kd_kernels.hpp", "kd_logits.hpp", "kd_topk.hpp",
+                            "kd_host.hip")]
 
 
 def naive_logit_bytes(T: int, V: int, itemsize: int = 2) -> int:
@@ -326,6 +327,7 @@ def main():
         res["seq_chunk"] = run_seq_chunk(args, wl, x)
     if not args.no_variants:
         res["logits_variant"] = run_logits_variant(args, wl, x)
+        res["topk_variant"] = res["logits_variant"].pop("topk_variant")
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(x, wl.tau, args.cpu_rows)
     else:
