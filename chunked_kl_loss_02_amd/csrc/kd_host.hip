@@ -95,8 +95,8 @@ Plan make_plan(const kd_problem* p, bool with_grad = true) {
   P.gt2 = env_int("KDKL_GROUP_T2", 4);
   P.gv1 = env_int("KDKL_GROUP_V1", 8);
   P.gv2 = env_int("KDKL_GROUP_V2", 8);
-  P.gm_dh = std::max(1, env_int("KDKL_GROUP_MDH", 4));
-  P.gm_dw = std::max(1, env_int("KDKL_GROUP_MDW", 2));
+  P.gm_dh = std::max(1, env_int("KDKL_GROUP_MDH", 6));
+  P.gm_dw = std::max(1, env_int("KDKL_GROUP_MDW", 4));
   if (P.gt1 < 1) P.gt1 = 1;
   if (P.gt2 < 1) P.gt2 = 1;
   P.ldp = (int64_t)P.ntt_max * 256;

@@ -410,24 +410,20 @@ __global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 
   LoaderKC<256> la, lb;
   la.init(a.W + (int64_t)vt * 256 * a.H, a.vrows - (int64_t)vt * 256, a.H);
   lb.init(a.h + (int64_t)tt * 256 * a.H, a.rows - (int64_t)tt * 256, a.H);
-  // per-token LSE and gradient coefficient of this lane's 4 token columns,
-  // fetched before the K loop so their latency is hidden
-  float l2v[4], cfv[4];
-  uint32_t sgn;  // sign bits of a negative coefficient, applied to the packed bf16 pairs
+  // Per token of the tile: |G| = |coef| 2^(c S - lse2) = 2^(c S - off) with
+  // off = lse2 - log2 |coef|; a masked or padding token (coef = 0) has an
+  // infinite offset and exact zeros.  The offsets are staged in LDS before
+  // the K loop (their loads overlap it, and they hold no registers there).
+  __shared__ float s_off[256];
+  const float cs = a.scal_f[0];
   {
-    const float cs = a.scal_f[0];
-    const float coef = fabsf(cs);
-    sgn = cs < 0.f ? 0x80008000u : 0u;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int t = tt * 256 + wn * 128 + acc_col(j, lane);
-      const bool tv = t < a.rows && (a.mask ? a.mask[t] != 0 : true);
-      l2v[j] = tv ? a.lse2[t] : 0.f;
-      cfv[j] = tv ? coef : 0.f;
-    }
+    const int t = tt * 256 + (int)threadIdx.x;
+    const bool tv = t < a.rows && (a.mask ? a.mask[t] != 0 : true) && cs != 0.f;
+    s_off[threadIdx.x] = tv ? a.lse2[t] - log2f(fabsf(cs)) : INFINITY;
   }
   f32x16 acc[4][4];
   gemm_tile<4, 4>(la, lb, (int)(a.H / kBK), st, acc);
+  const uint32_t sgn = cs < 0.f ? 0x80008000u : 0u;  // sign bits of a negative coefficient
   // The bf16 tile goes through LDS (the four stages, 4 x 32 KiB, are free
   // after gemm_tile; 64 token rows each) as [256 tokens][256 vocab] rows of
   // 32 16-byte chunks, chunk c of row t at position c ^ (t & 31), then leaves
@@ -436,16 +432,11 @@ __global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 
     uint16_t* b = tl < 64 ? st.a0 : tl < 128 ? st.a1 : tl < 192 ? st.b0 : st.b1;
     return b + (tl & 63) * 256;
   };
-  // |G| = |coef| 2^(c S - lse2) = 2^(c S - (lse2 - log2 |coef|)); a masked
-  // or padding token has coef = 0, i.e. an infinite offset and exact zeros
-  float offv[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) offv[j] = cfv[j] > 0.f ? l2v[j] - log2f(cfv[j]) : INFINITY;
   const bool full = (int64_t)vt * 256 + 256 <= a.vrows;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int tl = wn * 128 + acc_col(j, lane);  // token row inside the tile
-    const float off = offv[j];
+    const float off = s_off[tl];
     uint16_t* trow = row(tl);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
