@@ -46,6 +46,7 @@ struct Plan {
   // gradient outputs)
   bool seq;          // sequence-chunk schedule (stored logits of a token block)
   size_t o_S;        // seq: S^T of one block, [V, Tb] fp32
+  size_t o_hT;       // h^T of one token block, [H, Tb] bf16 (gradient pass)
   size_t o_G, o_dhs, o_dws, o_part, o_lse2, o_p, o_pm, o_s, o_neg, o_row, o_bsum, o_scal_f, o_scal_i, o_status, total;
 };
 
@@ -105,6 +106,7 @@ Plan make_plan(const kd_problem* p, bool with_grad = true) {
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t r = o; o += (bytes + 255) & ~size_t(255); return r; };
   P.o_G = with_grad ? take((size_t)P.grows * P.chunk_v * 2) : 0;
+  P.o_hT = with_grad ? take((size_t)P.H * P.Tb * 2) : 0;
   P.o_S = P.seq ? take((size_t)P.V * P.Tb * 4) : 0;
   const bool stage = with_grad && (p->flags & KD_FLAG_GRAD_BF16);
   // the sequence-chunk schedule finishes a dW chunk only after the last
@@ -184,6 +186,7 @@ struct Inputs {
 // per-token state (lse2, gathered logits) lives.
 struct Bufs {
   uint16_t* G;
+  uint16_t* hT;  // h^T of one token block (gradient pass)
   float* dhs;   // fp32 staging of a bf16 dH (nullable)
   float* dws;   // fp32 staging of one chunk of a bf16 dW (nullable)
   float2* part;
@@ -203,6 +206,7 @@ Bufs carve(const Plan& P, void* workspace, bool with_grad) {
   char* ws = static_cast<char*>(workspace);
   Bufs b{};
   b.G = with_grad ? reinterpret_cast<uint16_t*>(ws + P.o_G) : nullptr;
+  b.hT = with_grad ? reinterpret_cast<uint16_t*>(ws + P.o_hT) : nullptr;
   b.dhs = with_grad && P.o_dhs ? reinterpret_cast<float*>(ws + P.o_dhs) : nullptr;
   b.dws = with_grad && P.o_dws ? reinterpret_cast<float*>(ws + P.o_dws) : nullptr;
   b.part = reinterpret_cast<float2*>(ws + P.o_part);
@@ -290,6 +294,14 @@ void launch_forward(Launcher& L, const Plan& P, const Inputs& in, const Bufs& b,
   L.run(4, [&] { k_sum<<<1, 1024, 0, s>>>(b.bsum, nb, b.scal_f, loss); });
 }
 
+// h^T of the token block [t0, t0 + rows) into the workspace (the dW
+// contraction's operand), zero-padded to the block width.
+void launch_transpose_h(Launcher& L, const Plan& P, const Inputs& in, const Bufs& b, int64_t t0, int64_t rows) {
+  hipStream_t s = L.s;
+  const dim3 grid((unsigned)(P.Tb / 64), (unsigned)(P.H / 64));
+  L.run(8, [&] { kd::k_transpose_h<<<grid, 256, 0, s>>>(in.h + t0 * P.H, rows, P.H, b.hT, P.Tb); });
+}
+
 // Pass 2: recompute every (block, chunk), form the logit gradient, contract
 // it into dH / dW (fp32 or bf16 per the flags).
 void launch_backward(Launcher& L, const Plan& P, uint32_t flags, const Inputs& in, const Bufs& b, void* dH_out,
@@ -306,6 +318,9 @@ void launch_backward(Launcher& L, const Plan& P, uint32_t flags, const Inputs& i
   float* dH = dH_out ? (bf16 ? b.dhs : static_cast<float*>(dH_out)) : nullptr;
   float* dWc_stage = dW_out && bf16 ? b.dws : nullptr;
   const int nht = (int)cdiv(H, 256);
+  // one token block: its h^T is made once; otherwise before each contraction
+  const bool one_block = T <= P.Tb;
+  if (dW_out && one_block) launch_transpose_h(L, P, in, b, 0, T);
   int ci = 0;
   for (int64_t v0 = 0; v0 < V; v0 += P.chunk_v, ++ci) {
     const int64_t vrows = std::min<int64_t>(P.chunk_v, V - v0);
@@ -339,9 +354,11 @@ void launch_backward(Launcher& L, const Plan& P, uint32_t flags, const Inputs& i
                                                               b.lse2 + t0, in.mask ? in.mask + t0 : nullptr, b.scal_f,
                                                               rows, K, v0, vrows, c, b.G, P.chunk_v);
       });
+      if (dW_out && !one_block) launch_transpose_h(L, P, in, b, t0, rows);
       BwdArgs g{};
       g.W = in.W + v0 * H;
-      g.h = in.h + t0 * H;
+      g.hT = b.hT;
+      g.ldt = P.Tb;
       g.G = b.G;
       g.dH = dH ? dH + t0 * H : nullptr;
       g.dW = dW;
@@ -431,6 +448,7 @@ void launch_seq(Launcher& L, const Plan& P, uint32_t flags, const Inputs& in, co
                                                                b.s + t0 * K);
     });
     if (!dH_out && !dW_out) continue;
+    if (dW_out) launch_transpose_h(L, P, in, b, t0, rows);
     int ci = 0;
     for (int64_t v0 = 0; v0 < V; v0 += P.chunk_v, ++ci) {
       const int64_t vrows = std::min<int64_t>(P.chunk_v, V - v0);
@@ -457,7 +475,8 @@ void launch_seq(Launcher& L, const Plan& P, uint32_t flags, const Inputs& in, co
       if (dW_out) dW = bf16 ? (whole_dw ? b.dws + v0 * H : b.dws) : static_cast<float*>(dW_out) + v0 * H;
       BwdArgs g{};
       g.W = in.W + v0 * H;
-      g.h = in.h + t0 * H;
+      g.hT = b.hT;
+      g.ldt = P.Tb;
       g.G = b.G;
       g.dH = dH ? dH + t0 * H : nullptr;
       g.dW = dW;

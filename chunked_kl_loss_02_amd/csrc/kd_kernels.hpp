@@ -556,15 +556,46 @@ __global__ void __launch_bounds__(256) k_sgrad(SgradArgs a) {
   }
 }
 
+// h^T of one token block: hT[m, t] = h[t0 + t, m] for t < rows, zero for
+// rows <= t < ldt (the padded block), so that the dW contraction reads its h
+// operand k-contiguous.  A workgroup moves a 64 (token) x 64 (hidden) tile
+// through LDS: 16-byte reads along the hidden axis, 4-byte writes (two
+// tokens) along the token axis.  Grid: (ldt / 64, H / 64).
+__global__ void __launch_bounds__(256) k_transpose_h(const uint16_t* __restrict__ h, int64_t rows, int64_t H,
+                                                      uint16_t* __restrict__ hT, int64_t ldt) {
+  __shared__ uint16_t tile[64][66];  // [token][hidden], two spare columns of bank skew
+  const int64_t t0 = (int64_t)blockIdx.x * 64, m0 = (int64_t)blockIdx.y * 64;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int e = tid; e < 64 * 8; e += 256) {
+    const int t = e >> 3, c = e & 7;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (t0 + t < rows) v = *reinterpret_cast<const u32x4*>(h + (t0 + t) * H + m0 + c * 8);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      tile[t][c * 8 + 2 * q] = (uint16_t)(v[q] & 0xFFFFu);
+      tile[t][c * 8 + 2 * q + 1] = (uint16_t)(v[q] >> 16);
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int e = tid; e < 64 * 32; e += 256) {
+    const int m = e >> 5, q = e & 31;  // hidden row, token pair
+    const uint32_t x = (uint32_t)tile[2 * q][m] | ((uint32_t)tile[2 * q + 1][m] << 16);
+    *reinterpret_cast<uint32_t*>(hT + (m0 + m) * ldt + t0 + 2 * q) = x;
+  }
+}
+
 // dH (over the chunk's vocabulary) and dW (over the block's tokens) from G.
 // Work ids [0, ndh) are dH tiles (hidden tile x token tile, K = vocabulary);
 // the rest are dW tiles (hidden tile x vocabulary tile, K = tokens).  Both
 // are computed transposed so that a lane stores 4 consecutive hidden units:
 //   dH^T[m, t] = sum_v W[v, m] G[t, v]      (W rows read with transposed LDS reads)
-//   dW^T[m, v] = sum_t h[t, m] G[t, v]      (h and G rows read with transposed LDS reads)
+//   dW^T[m, v] = sum_t hT[m, t] G[t, v]     (G rows read with transposed LDS reads)
 struct BwdArgs {
   const uint16_t* W;      // chunk origin [vrows, H]
-  const uint16_t* h;      // block origin [rows, H]
+  const uint16_t* hT;     // the block's h^T [H, ldt] (k_transpose_h)
+  int64_t ldt;
   const uint16_t* G;      // [*, ldg]
   float* dH;              // block origin [rows, H] (nullable)
   float* dW;              // chunk origin [vrows, H] (nullable)
@@ -604,8 +635,9 @@ __global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 
     const int id = xcd_remap(L - a.ndh_pad, a.ndw_pad);
     if (id >= a.ndw) return;
     grouped(id, a.nht, a.nvt, a.gm_dw, mt, nt);
-    LoaderTR la, lb;
-    la.init(a.h, a.rows, a.H, mt * 256);
+    LoaderKC<256> la;
+    LoaderTR lb;
+    la.init(a.hT + (int64_t)mt * 256 * a.ldt, a.H - (int64_t)mt * 256, a.ldt);
     lb.init(a.G, a.grows, a.ldg, nt * 256);
     gemm_tile<4, 4>(la, lb, (int)((a.rows + kBK - 1) / kBK), st, acc);
     out = a.dW;

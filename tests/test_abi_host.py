@@ -51,8 +51,9 @@ def _ws(T, H, V, K, tau=1.0, chunk_v=0, block_t=0):
 def test_workspace_plan():
     code, n = _ws(4096, 2880, 201088, 64)
     assert code == 0
-    # gradient buffer (4096 x 16384 bf16) plus per-token state
-    fixed = 4096 * 16384 * 2
+    # gradient buffer (4096 x 16384 bf16), the block's h^T (2880 x 4096 bf16)
+    # plus per-token state
+    fixed = 4096 * 16384 * 2 + 2880 * 4096 * 2
     assert fixed <= n < fixed + 4096 * 8 * 1024
     # per-token growth is linear once T exceeds one block
     _, a = _ws(65536, 2880, 201088, 64)
@@ -131,8 +132,8 @@ def test_split_entry_point_sizes():
     assert code == 0
     code, fwd = _size(L.kd_topk_kl_fwd_workspace_size, T, H, V, K)
     assert code == 0
-    # the forward needs no gradient buffer (4096 x 16384 bf16)
-    assert full - fwd == 4096 * 16384 * 2
+    # the forward needs no gradient buffer (4096 x 16384 bf16) and no h^T (2880 x 4096 bf16)
+    assert full - fwd == 4096 * 16384 * 2 + H * 4096 * 2
     code, saved = _size(L.kd_topk_kl_saved_size, T, H, V, K)
     assert code == 0
     # log-sum-exp [T] and the gathered logits [T, K], fp32, 256-byte aligned pieces
