@@ -25,7 +25,7 @@ KD_FLAG_ACCUMULATE_DH = 2
 KD_FLAG_ACCUMULATE_DW = 4
 KD_FLAG_GRAD_BF16 = 8
 KD_FLAG_SEQ_CHUNK = 16
-ABI_VERSION = 3
+ABI_VERSION = 4
 KD_FLAG_LOGITS_F32 = 32
 KERNEL_CLASSES = ("teacher", "gather", "pass1", "lse", "loss", "pass2", "fixup", "bwd", "other", "logits", "topk")
 _STATUS = {0: "KD_OK", 1: "KD_ERR_ARG", 2: "KD_ERR_UNSUPPORTED", 3: "KD_ERR_WORKSPACE",
@@ -88,6 +88,8 @@ def lib():
     L.kd_timing_enable.restype = ctypes.c_int
     L.kd_timing_collect.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
     L.kd_timing_collect.restype = ctypes.c_int
+    L.kd_timing_classes.argtypes = [ctypes.c_uint32]
+    L.kd_timing_classes.restype = ctypes.c_int
     LP = ctypes.POINTER(KdLogitsProblem)
     L.kd_topk_kl_logits_workspace_size.argtypes = [LP, ctypes.POINTER(sz)]
     L.kd_topk_kl_logits_workspace_size.restype = ctypes.c_int
@@ -347,7 +349,15 @@ def lse(workspace, T, H, V, K, tau=1.0, chunk_v=0, block_t=0, flags=0):
     return workspace[off:off + 4 * T].view(torch.float32) * 0.6931471805599453
 
 
-def timing_enable(on=True):
+def timing_enable(on=True, classes=None):
+    """Per-kernel HIP-event timing on or off; classes: names from
+    KERNEL_CLASSES to time (None: all), the others record no events."""
+    mask = 0xFFFFFFFF
+    if classes is not None:
+        mask = 0
+        for c in classes:
+            mask |= 1 << KERNEL_CLASSES.index(c)
+    _raise(lib().kd_timing_classes(mask))
     _raise(lib().kd_timing_enable(1 if on else 0))
 
 

@@ -135,6 +135,7 @@ struct TimedLaunch {
   hipEvent_t a, b;
 };
 bool g_timing = false;
+uint32_t g_timing_mask = ~0u;
 constexpr int kTimingClasses = 11;
 std::vector<TimedLaunch> g_launches;
 std::vector<hipEvent_t> g_pool;
@@ -157,7 +158,8 @@ struct Launcher {
   void run(int cls, F&& f) {
     if (err != hipSuccess) return;
     hipEvent_t a = nullptr, b = nullptr;
-    if (g_timing) {
+    const bool timed = g_timing && ((g_timing_mask >> cls) & 1u);
+    if (timed) {
       a = pool_get();
       b = pool_get();
       if (a) (void)hipEventRecord(a, s);
@@ -165,7 +167,7 @@ struct Launcher {
     f();
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) err = e;
-    if (g_timing && a && b) {
+    if (timed && a && b) {
       (void)hipEventRecord(b, s);
       g_launches.push_back({cls, a, b});
     }
@@ -548,7 +550,7 @@ kd_status finish(Launcher& L, bool validate, const uint32_t* status) {
 
 extern "C" {
 
-int kd_abi_version(void) { return 3; }
+int kd_abi_version(void) { return 4; }
 
 const char* kd_status_string(kd_status s) {
   switch (s) {
@@ -579,6 +581,11 @@ const float* kd_topk_kl_workspace_lse2(const kd_problem* p, const void* workspac
 
 kd_status kd_timing_enable(int on) {
   g_timing = on != 0;
+  return KD_OK;
+}
+
+kd_status kd_timing_classes(uint32_t mask) {
+  g_timing_mask = mask;
   return KD_OK;
 }
 

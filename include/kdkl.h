@@ -218,7 +218,8 @@ const char* kd_status_string(kd_status s);
 
 /* ABI version (incremented on any change of the declarations above; 2 adds
  * the split forward / backward entry points and the gradient flags, 3 the
- * logits variant, the top-K selection and two more timing classes). */
+ * logits variant, the top-K selection and two more timing classes, 4 the
+ * timing class mask). */
 int kd_abi_version(void);
 
 /* Optional per-kernel timing with HIP events recorded on the launch stream
@@ -231,6 +232,11 @@ int kd_abi_version(void);
  * be NULL) and releases the events. */
 kd_status kd_timing_enable(int on);
 kd_status kd_timing_collect(double* ms, int64_t* launches);
+/* Restricts the timing to the classes whose bit (1 << class) is set in mask
+ * (default: all); the other launches record no events, so that timing one
+ * kernel adds no event traffic between the rest.  Bits of unknown classes
+ * are ignored. */
+kd_status kd_timing_classes(uint32_t mask);
 
 #ifdef __cplusplus
 }

@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol():
     L = kd.lib()
     for n in declared_functions():
         assert hasattr(L, n)
-    assert L.kd_abi_version() == kd.ABI_VERSION == 3
+    assert L.kd_abi_version() == kd.ABI_VERSION == 4
 
 
 def _ws(T, H, V, K, tau=1.0, chunk_v=0, block_t=0):
