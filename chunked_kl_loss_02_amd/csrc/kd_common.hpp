@@ -34,10 +34,14 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
   return __builtin_bit_cast(float, bits16 << 16);
 }
 // round-to-nearest-even (v_cvt_pk_bf16_f32 on gfx950)
+// Two floats to bf16 (round to nearest even), lo in the low half.  The
+// vector conversion selects one v_cvt_pk_bf16_f32 with both sources (two
+// scalar casts would convert one lane each and need a shift and a merge).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  uint16_t a = __builtin_bit_cast(uint16_t, (__bf16)lo);
-  uint16_t b = __builtin_bit_cast(uint16_t, (__bf16)hi);
-  return (uint32_t)a | ((uint32_t)b << 16);
+  typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+  typedef float f32x2v __attribute__((ext_vector_type(2)));
+  const f32x2v f = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2v));
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

@@ -75,7 +75,8 @@ struct LoaderKC {
 #pragma unroll
     for (int j = 0; j < NQ; ++j) {
       uint16_t* dst = s + (w * NQ + j) * 8 * kBK;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)dst, 16, voff[j], kt * (kBK * 2), 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)dst, 16, voff[j],
+                                               __builtin_amdgcn_readfirstlane(kt * (kBK * 2)), 0, 0);
     }
   }
   __device__ __forceinline__ void load(int) {}
@@ -312,21 +313,24 @@ __device__ __forceinline__ void gemm_tile(LA& la, LB& lb, int nk, const Stages& 
     for (int j = 0; j < NI; ++j) acc[i][j] = f32x16{};
   if (nk <= 0) return;
   bf16x8 a[2][MI], b[2][NI];
-  la.issue(0, st.a0);
-  lb.issue(0, st.b0);
+  // an odd step count starts in the second half of the loop body (step 0 in
+  // stage 1), so that one loop body, with no separate tail, runs every step
+  const bool odd = nk & 1;
+  uint16_t* sa = odd ? st.a1 : st.a0;
+  uint16_t* sb = odd ? st.b1 : st.b0;
+  la.issue(0, sa);
+  lb.issue(0, sb);
   la.load(0);
   lb.load(0);
-  la.store(st.a0);
-  lb.store(st.b0);
+  la.store(sa);
+  lb.store(sb);
   wait_all();
   __syncthreads();
-  load_frags<MI, NI, LA, LB>(st.a0, st.b0, a[0], b[0], arow0, brow0, lane, 0);
-  int kt = 0;
-  for (; kt + 1 < nk; kt += 2) {
-    kstep<MI, NI>(la, lb, kt + 1, st.a0, st.b0, st.a1, st.b1, acc, a, b, arow0, brow0, lane);
+  load_frags<MI, NI, LA, LB>(sa, sb, a[0], b[0], arow0, brow0, lane, 0);
+  for (int kt = odd ? -1 : 0; kt + 1 < nk; kt += 2) {
+    if (kt >= 0) kstep<MI, NI>(la, lb, kt + 1, st.a0, st.b0, st.a1, st.b1, acc, a, b, arow0, brow0, lane);
     kstep<MI, NI>(la, lb, kt + 2 < nk ? kt + 2 : kt + 1, st.a1, st.b1, st.a0, st.b0, acc, a, b, arow0, brow0, lane);
   }
-  if (kt < nk) kstep<MI, NI>(la, lb, kt, st.a0, st.b0, st.a1, st.b1, acc, a, b, arow0, brow0, lane);
   // the last region read the idle stage's first fragments: let every wave
   // finish its LDS reads before anyone reuses the stages
   wait_all();

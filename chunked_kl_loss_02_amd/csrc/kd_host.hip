@@ -47,6 +47,7 @@ struct Plan {
   bool seq;          // sequence-chunk schedule (stored logits of a token block)
   size_t o_S;        // seq: S^T of one block, [V, Tb] fp32
   size_t o_hT;       // h^T of one token block, [H, Tb] bf16 (gradient pass)
+  size_t o_off;      // per-token pass-2 offsets [Tp] (gradient pass)
   size_t o_G, o_dhs, o_dws, o_part, o_lse2, o_p, o_pm, o_s, o_neg, o_row, o_bsum, o_scal_f, o_scal_i, o_status, total;
 };
 
@@ -107,6 +108,7 @@ Plan make_plan(const kd_problem* p, bool with_grad = true) {
   auto take = [&](size_t bytes) { size_t r = o; o += (bytes + 255) & ~size_t(255); return r; };
   P.o_G = with_grad ? take((size_t)P.grows * P.chunk_v * 2) : 0;
   P.o_hT = with_grad ? take((size_t)P.H * P.Tb * 2) : 0;
+  P.o_off = with_grad ? take((size_t)Tp * 4) : 0;
   P.o_S = P.seq ? take((size_t)P.V * P.Tb * 4) : 0;
   const bool stage = with_grad && (p->flags & KD_FLAG_GRAD_BF16);
   // the sequence-chunk schedule finishes a dW chunk only after the last
@@ -189,6 +191,7 @@ struct Inputs {
 struct Bufs {
   uint16_t* G;
   uint16_t* hT;  // h^T of one token block (gradient pass)
+  float* off;    // pass-2 offsets (gradient pass)
   float* dhs;   // fp32 staging of a bf16 dH (nullable)
   float* dws;   // fp32 staging of one chunk of a bf16 dW (nullable)
   float2* part;
@@ -209,6 +212,7 @@ Bufs carve(const Plan& P, void* workspace, bool with_grad) {
   Bufs b{};
   b.G = with_grad ? reinterpret_cast<uint16_t*>(ws + P.o_G) : nullptr;
   b.hT = with_grad ? reinterpret_cast<uint16_t*>(ws + P.o_hT) : nullptr;
+  b.off = with_grad ? reinterpret_cast<float*>(ws + P.o_off) : nullptr;
   b.dhs = with_grad && P.o_dhs ? reinterpret_cast<float*>(ws + P.o_dhs) : nullptr;
   b.dws = with_grad && P.o_dws ? reinterpret_cast<float*>(ws + P.o_dws) : nullptr;
   b.part = reinterpret_cast<float2*>(ws + P.o_part);
@@ -320,6 +324,10 @@ void launch_backward(Launcher& L, const Plan& P, uint32_t flags, const Inputs& i
   float* dH = dH_out ? (bf16 ? b.dhs : static_cast<float*>(dH_out)) : nullptr;
   float* dWc_stage = dW_out && bf16 ? b.dws : nullptr;
   const int nht = (int)cdiv(H, 256);
+  const int64_t Tp = align256(T);
+  L.run(8, [&] {
+    k_offsets<<<(unsigned)cdiv(Tp, 256), 256, 0, s>>>(b.lse2, in.mask, T, Tp, b.scal_f, b.off);
+  });
   // one token block: its h^T is made once; otherwise before each contraction
   const bool one_block = T <= P.Tb;
   if (dW_out && one_block) launch_transpose_h(L, P, in, b, 0, T);
@@ -335,8 +343,7 @@ void launch_backward(Launcher& L, const Plan& P, uint32_t flags, const Inputs& i
       Pass2Args a{};
       a.W = in.W + v0 * H;
       a.h = in.h + t0 * H;
-      a.lse2 = b.lse2 + t0;
-      a.mask = in.mask ? in.mask + t0 : nullptr;
+      a.off = b.off + t0;
       a.scal_f = b.scal_f;
       a.G = b.G;
       a.vrows = vrows;

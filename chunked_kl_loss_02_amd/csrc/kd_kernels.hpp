@@ -384,11 +384,24 @@ __global__ void __launch_bounds__(1024) k_sum(const double* __restrict__ bsum, i
 // One (token block, vocabulary chunk): G[t, v] = coef_t 2^(c S[t,v] - lse2[t])
 // in bf16 for every (t, v) of the padded tile grid (zero outside the valid
 // range or on masked tokens).
+// off[t] = lse2[t] - log2 |coef| for a kept token, +inf for a masked token,
+// for t past T (up to the 256-aligned end) and for coef = 0: pass 2 forms
+// |G| = |coef| 2^(c S - lse2) as 2^(c S - off), so the dropped tokens get
+// exact zeros.
+__global__ void __launch_bounds__(256) k_offsets(const float* __restrict__ lse2, const uint8_t* __restrict__ mask,
+                                                 int64_t T, int64_t Tp, const float* __restrict__ scal_f,
+                                                 float* __restrict__ off) {
+  const int64_t t = blockIdx.x * (int64_t)256 + threadIdx.x;
+  if (t >= Tp) return;
+  const float cs = scal_f[0];
+  const bool kept = t < T && (mask ? mask[t] != 0 : true) && cs != 0.f;
+  off[t] = kept ? lse2[t] - log2f(fabsf(cs)) : INFINITY;
+}
+
 struct Pass2Args {
   const uint16_t* W;      // chunk origin [V - v0, H]
   const uint16_t* h;      // block origin
-  const float* lse2;      // block origin
-  const uint8_t* mask;    // block origin (nullable)
+  const float* off;       // block origin (k_offsets), 256-aligned length
   const float* scal_f;
   uint16_t* G;            // [ntt*256, ldg]
   int64_t vrows, H, rows; // valid vocabulary rows in chunk / tokens in block
@@ -410,17 +423,17 @@ __global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 
   LoaderKC<256> la, lb;
   la.init(a.W + (int64_t)vt * 256 * a.H, a.vrows - (int64_t)vt * 256, a.H);
   lb.init(a.h + (int64_t)tt * 256 * a.H, a.rows - (int64_t)tt * 256, a.H);
-  // Per token of the tile: |G| = |coef| 2^(c S - lse2) = 2^(c S - off) with
-  // off = lse2 - log2 |coef|; a masked or padding token (coef = 0) has an
-  // infinite offset and exact zeros.  The offsets are staged in LDS before
-  // the K loop (their loads overlap it, and they hold no registers there).
-  __shared__ float s_off[256];
-  const float cs = a.scal_f[0];
+  // The tile's 256 token offsets (|G| = 2^(c S - off), k_offsets) go global
+  // -> LDS with one 4-byte-per-lane buffer load per wave: no registers held
+  // and no wait before the K loop, whose final wait and barrier cover them.
+  __shared__ __attribute__((aligned(16))) float s_off[256];
   {
-    const int t = tt * 256 + (int)threadIdx.x;
-    const bool tv = t < a.rows && (a.mask ? a.mask[t] != 0 : true) && cs != 0.f;
-    s_off[threadIdx.x] = tv ? a.lse2[t] - log2f(fabsf(cs)) : INFINITY;
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.off + (int64_t)tt * 256, 256 * 4);
+    const int wv = __builtin_amdgcn_readfirstlane(w);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(s_off + 64 * wv), 4, (uint32_t)threadIdx.x * 4u, 0, 0,
+                                             0);
   }
+  const float cs = a.scal_f[0];
   f32x16 acc[4][4];
   gemm_tile<4, 4>(la, lb, (int)(a.H / kBK), st, acc);
   const uint32_t sgn = cs < 0.f ? 0x80008000u : 0u;  // sign bits of a negative coefficient
@@ -432,7 +445,6 @@ __global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 
     uint16_t* b = tl < 64 ? st.a0 : tl < 128 ? st.a1 : tl < 192 ? st.b0 : st.b1;
     return b + (tl & 63) * 256;
   };
-  const bool full = (int64_t)vt * 256 + 256 <= a.vrows;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int tl = wn * 128 + acc_col(j, lane);  // token row inside the tile
@@ -446,11 +458,6 @@ __global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 
         float g[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) g[r] = fast_exp2(fmaf(acc[i][j][4 * q + r], a.c, -off));
-        if (!full) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if ((int64_t)vt * 256 + vr + r >= a.vrows) g[r] = 0.f;
-        }
         u32x2 pk;
         pk[0] = pack_bf16x2(g[0], g[1]) ^ sgn;
         pk[1] = pack_bf16x2(g[2], g[3]) ^ sgn;
@@ -459,12 +466,29 @@ __global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 
       }
   }
   __syncthreads();
+  // vocabulary columns past the chunk's valid rows leave as zeros (only in
+  // the chunk's last tile)
+  const int lim = (int)min<int64_t>(256, a.vrows - (int64_t)vt * 256);
   const int tid = threadIdx.x;
+  if (lim == 256) {
 #pragma unroll 4
-  for (int e = tid; e < 256 * 32; e += 256) {
-    const int tl = e >> 5, c = e & 31;
-    const u32x4 v = *reinterpret_cast<const u32x4*>(row(tl) + ((c ^ (tl & 31)) * 8));
-    *reinterpret_cast<u32x4*>(a.G + (int64_t)(tt * 256 + tl) * a.ldg + vt * 256 + c * 8) = v;
+    for (int e = tid; e < 256 * 32; e += 256) {
+      const int tl = e >> 5, c = e & 31;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(row(tl) + ((c ^ (tl & 31)) * 8));
+      *reinterpret_cast<u32x4*>(a.G + (int64_t)(tt * 256 + tl) * a.ldg + vt * 256 + c * 8) = v;
+    }
+  } else {
+    for (int e = tid; e < 256 * 32; e += 256) {
+      const int tl = e >> 5, c = e & 31;
+      u32x4 v = *reinterpret_cast<const u32x4*>(row(tl) + ((c ^ (tl & 31)) * 8));
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int col = c * 8 + 2 * q;
+        if (col >= lim) v[q] = 0u;
+        else if (col + 1 >= lim) v[q] &= 0xFFFFu;
+      }
+      *reinterpret_cast<u32x4*>(a.G + (int64_t)(tt * 256 + tl) * a.ldg + vt * 256 + c * 8) = v;
+    }
   }
 }
 

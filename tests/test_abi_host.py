@@ -132,8 +132,9 @@ def test_split_entry_point_sizes():
     assert code == 0
     code, fwd = _size(L.kd_topk_kl_fwd_workspace_size, T, H, V, K)
     assert code == 0
-    # the forward needs no gradient buffer (4096 x 16384 bf16) and no h^T (2880 x 4096 bf16)
-    assert full - fwd == 4096 * 16384 * 2 + H * 4096 * 2
+    # the forward needs no gradient buffer (4096 x 16384 bf16), no h^T (2880 x 4096 bf16)
+    # and no per-token pass-2 offsets (4096 fp32)
+    assert full - fwd == 4096 * 16384 * 2 + H * 4096 * 2 + 4 * 4096
     code, saved = _size(L.kd_topk_kl_saved_size, T, H, V, K)
     assert code == 0
     # log-sum-exp [T] and the gathered logits [T, K], fp32, 256-byte aligned pieces
