@@ -35,7 +35,7 @@ struct Plan {
   int64_t Tb;        // tokens per block
   int ntt_max;       // token tiles in a full block
   int64_t nvt;       // vocabulary tiles of 256
-  int per, nranges;  // pass 1: vocabulary tiles per workgroup, ranges
+  int nranges;       // pass 1: partial (max, sum) rows, one per vocabulary tile
   int gt1, gt2;      // token-tile group sizes of pass 1 / pass 2
   int gv1, gv2;      // vocabulary group sizes (take precedence when > 0)
   int gm_dh, gm_dw;  // hidden-tile group sizes of the gradient contractions
@@ -90,9 +90,7 @@ Plan make_plan(const kd_problem* p, bool with_grad = true) {
   if (P.Tb == 0) P.Tb = 256;
   P.ntt_max = (int)(P.Tb / 256);
   P.nvt = cdiv(P.V, 256);
-  P.per = env_int("KDKL_PASS1_PER", 1);
-  if (P.per < 1) P.per = 1;
-  P.nranges = (int)cdiv(P.nvt, P.per);
+  P.nranges = (int)P.nvt;
   P.gt1 = env_int("KDKL_GROUP_T1", 4);
   P.gt2 = env_int("KDKL_GROUP_T2", 4);
   P.gv1 = env_int("KDKL_GROUP_V1", 8);
@@ -279,11 +277,9 @@ void launch_forward(Launcher& L, const Plan& P, const Inputs& in, const Bufs& b,
     a.rows = rows;
     a.ntt = (int)cdiv(rows, 256);
     a.nvt = (int)P.nvt;
-    a.per = P.per;
-    a.nranges = P.nranges;
     a.gt = std::min(P.gt1, a.ntt);
-    a.gv = std::min(P.gv1, a.nranges);
-    a.total = a.ntt * a.nranges;
+    a.gv = std::min(P.gv1, a.nvt);
+    a.total = a.ntt * a.nvt;
     a.ldp = (int)P.ldp;
     a.c = c;
     const int grid = (int)(cdiv(a.total, 8) * 8);
@@ -437,11 +433,9 @@ void launch_seq(Launcher& L, const Plan& P, uint32_t flags, const Inputs& in, co
     a.rows = rows;
     a.ntt = ntt;
     a.nvt = (int)P.nvt;
-    a.per = P.per;
-    a.nranges = P.nranges;
     a.gt = std::min(P.gt1, a.ntt);
-    a.gv = std::min(P.gv1, a.nranges);
-    a.total = a.ntt * a.nranges;
+    a.gv = std::min(P.gv1, a.nvt);
+    a.total = a.ntt * a.nvt;
     a.ldp = (int)P.ldp;
     a.c = c;
     a.St = St;

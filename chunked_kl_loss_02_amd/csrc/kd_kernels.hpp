@@ -185,9 +185,9 @@ __global__ void __launch_bounds__(256) k_gather(const uint16_t* __restrict__ h, 
 struct Pass1Args {
   const uint16_t* W;     // [V, H]
   const uint16_t* h;     // token block origin [rows, H]
-  float2* part;          // [nranges, ldp]
+  float2* part;          // [nvt, ldp]: (max, sum) per vocabulary tile and token
   int64_t V, H, rows;    // rows = valid tokens in the block
-  int ntt, nvt, per, nranges, gt, gv, total, ldp;  // gv > 0: group vocabulary ranges instead
+  int ntt, nvt, gt, gv, total, ldp;  // gv > 0: group vocabulary tiles instead
   float c;               // log2(e) / tau
   float* St;             // kStore: S^T of the block, [V rows, lds] fp32 (row v, column t)
   int64_t lds;
@@ -237,63 +237,59 @@ __device__ __forceinline__ void store_tile_t(const Pass1Args& a, const Stages& s
   }
 }
 
-// kStore additionally writes the tile's logits (store_tile_t).
+// One (token tile, vocabulary tile) per workgroup: S^T of the tile, then per
+// token the tile's max m and sum l of 2^(c S - m) (base-2 log-sum-exp parts),
+// folded across tiles by k_lse.  Nothing but the loaders lives across the K
+// loop.  kStore additionally writes the tile's logits (store_tile_t).
 template <bool kStore>
 __global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) k_pass1(Pass1Args a) {
   KD_DECLARE_STAGES(st, 256, 256);
   __shared__ float2 red[2][128];
   const int id = xcd_remap(blockIdx.x, gridDim.x);
   if (id >= a.total) return;
-  int tt, vr;
+  int tt, vt;
   if (a.gv > 0)
-    grouped(id, a.nranges, a.ntt, a.gv, vr, tt);
+    grouped(id, a.nvt, a.ntt, a.gv, vt, tt);
   else
-    grouped(id, a.ntt, a.nranges, a.gt, tt, vr);
+    grouped(id, a.ntt, a.nvt, a.gt, tt, vt);
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int wm = w & 1, wn = w >> 1;
-  const int nk = (int)(a.H / kBK);
-  const int vt0 = vr * a.per, vt1 = min(a.nvt, vt0 + a.per);
-
-  LoaderKC<256> lb;
-  lb.init(a.h + (int64_t)tt * 256 * a.H, a.rows - (int64_t)tt * 256, a.H);
+  f32x16 acc[4][4];
+  {
+    LoaderKC<256> la, lb;
+    la.init(a.W + (int64_t)vt * 256 * a.H, a.V - (int64_t)vt * 256, a.H);
+    lb.init(a.h + (int64_t)tt * 256 * a.H, a.rows - (int64_t)tt * 256, a.H);
+    gemm_tile<4, 4>(la, lb, (int)(a.H / kBK), st, acc);
+  }
+  // vocabulary rows of this lane: vt*256 + wm*128 + acc_row(i, e)
+  const int64_t vbase = (int64_t)vt * 256 + wm * 128;
+  if constexpr (kStore) store_tile_t(a, st, acc, vt, tt, wm, wn, lane);
+  if (vbase + 128 > a.V) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        if (vbase + acc_row(i, e, lane) >= a.V)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[i][j][e] = -INFINITY;
+  }
   float rm[4], rl[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) { rm[j] = -INFINITY; rl[j] = 0.f; }
-  f32x16 acc[4][4];
-  for (int vt = vt0; vt < vt1; ++vt) {
-    LoaderKC<256> la;
-    la.init(a.W + (int64_t)vt * 256 * a.H, a.V - (int64_t)vt * 256, a.H);
-    gemm_tile<4, 4>(la, lb, nk, st, acc);
-    // vocabulary rows of this lane: vt*256 + wm*128 + acc_row(i, e)
-    const int64_t vbase = (int64_t)vt * 256 + wm * 128;
-    if constexpr (kStore) store_tile_t(a, st, acc, vt, tt, wm, wn, lane);
-    const bool ragged = vbase + 128 > a.V;
-    if (ragged) {
+  for (int j = 0; j < 4; ++j) {
+    float mx = -INFINITY;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int e = 0; e < 16; ++e)
-          if (vbase + acc_row(i, e, lane) >= a.V)
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, acc[i][j][e]);
+    const float m = mx * a.c;
+    const float ref = m == -INFINITY ? 0.f : m;  // rows of this lane all past V
+    float sum = 0.f;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) acc[i][j][e] = -INFINITY;
-    }
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, acc[i][j][e]);
-      const float nm = fmaxf(rm[j], mx * a.c);
-      const float ref = nm == -INFINITY ? 0.f : nm;  // rows of this lane all past V
-      float sum = 0.f;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) sum += fast_exp2(fmaf(acc[i][j][e], a.c, -ref));
-      rl[j] = rl[j] * fast_exp2(rm[j] - ref) + sum;
-      rm[j] = nm;
-    }
+      for (int e = 0; e < 16; ++e) sum += fast_exp2(fmaf(acc[i][j][e], a.c, -ref));
+    rm[j] = m;
+    rl[j] = sum;
   }
   // merge the two lane halves (same token, other vocabulary rows)
 #pragma unroll
@@ -314,12 +310,12 @@ __global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 
       const float2 o = red[wn][acc_col(j, lane)];
       lse_merge(rm[j], rl[j], o.x, o.y);
       const int t = tt * 256 + wn * 128 + acc_col(j, lane);
-      a.part[(int64_t)vr * a.ldp + t] = make_float2(rm[j], rl[j]);
+      a.part[(int64_t)vt * a.ldp + t] = make_float2(rm[j], rl[j]);
     }
   }
 }
 
-// lse2[t] = log2 sum_v 2^(c S[t,v]) from the per-range partials.  A block
+// lse2[t] = log2 sum_v 2^(c S[t,v]) from the per-tile partials.  A block
 // handles 32 tokens; its 8 thread groups each fold every 8th range, then the
 // 8 partial results are folded in a fixed order (deterministic).
 __global__ void __launch_bounds__(256) k_lse(const float2* __restrict__ part, int nranges, int ldp, int64_t rows,
