@@ -14,7 +14,8 @@
 
 namespace {
 
-constexpr int kDefaultChunkV = 16384;
+constexpr int kDefaultChunkV = 12288;
+constexpr int kDefaultSeqChunkV = 16384;  // measured best for the sequence-chunk schedule
 constexpr int kDefaultBlockT = 16384;
 constexpr int kDefaultSeqBlockT = 4096;
 
@@ -65,7 +66,7 @@ kd_status check(const kd_problem* p) {
   if (p->K > kd::kTeacherMaxK) return KD_ERR_UNSUPPORTED;
   if (p->chunk_v % 256 != 0 || p->block_t % 256 != 0) return KD_ERR_UNSUPPORTED;
   if (p->V > (int64_t)INT32_MAX || p->T > ((int64_t)1 << 40)) return KD_ERR_UNSUPPORTED;
-  const int64_t cv = p->chunk_v ? p->chunk_v : kDefaultChunkV;
+  const int64_t cv = p->chunk_v ? p->chunk_v : std::max(kDefaultChunkV, kDefaultSeqChunkV);
   const int64_t bt = p->block_t ? p->block_t : kDefaultBlockT;
   // 32-bit buffer offsets inside one chunk / block operand
   const int64_t lim = (int64_t)UINT32_MAX;
@@ -83,8 +84,8 @@ Plan make_plan(const kd_problem* p, bool with_grad = true) {
   P.V = p->V;
   P.K = p->K;
   P.tau = p->tau;
-  P.chunk_v = p->chunk_v ? p->chunk_v : kDefaultChunkV;
   P.seq = with_grad && (p->flags & KD_FLAG_SEQ_CHUNK);
+  P.chunk_v = p->chunk_v ? p->chunk_v : P.seq ? kDefaultSeqChunkV : kDefaultChunkV;
   P.block_t = p->block_t ? p->block_t : P.seq ? kDefaultSeqBlockT : kDefaultBlockT;
   P.Tb = P.T < P.block_t ? align256(P.T) : P.block_t;
   if (P.Tb == 0) P.Tb = 256;

@@ -24,8 +24,8 @@
  *
  * Memory: besides the caller's inputs and outputs the library touches only
  * the caller's workspace (see kd_topk_kl_workspace_size): a fixed
- * block_t x chunk_v bf16 gradient buffer plus O(T*K + T*V/(256*per)) per-token
- * state.  It allocates no device memory, keeps no state between calls (except
+ * block_t x chunk_v bf16 gradient buffer, h^T of one token block (H x
+ * block_t bf16) plus O(T*K + T*V/256) per-token state.  It allocates no device memory, keeps no state between calls (except
  * the optional timing facility below) and is reentrant across streams given
  * distinct workspaces.
  */
@@ -80,7 +80,8 @@ typedef struct kd_problem {
   int64_t V;        /* vocabulary size; >= 1 */
   int32_t K;        /* cached teacher entries per token; 1 <= K <= min(V, 1024) */
   float tau;        /* temperature; finite, > 0 */
-  int32_t chunk_v;  /* vocabulary chunk of the gradient pass; 0 = 16384; multiple of 256 */
+  int32_t chunk_v;  /* vocabulary chunk of the gradient pass; 0 = 12288 (16384 with
+                       KD_FLAG_SEQ_CHUNK); multiple of 256 */
   int32_t block_t;  /* token block of both passes; 0 = 16384; multiple of 256 */
   uint32_t flags;   /* KD_FLAG_* */
 } kd_problem;

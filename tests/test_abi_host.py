@@ -51,9 +51,9 @@ def _ws(T, H, V, K, tau=1.0, chunk_v=0, block_t=0):
 def test_workspace_plan():
     code, n = _ws(4096, 2880, 201088, 64)
     assert code == 0
-    # gradient buffer (4096 x 16384 bf16), the block's h^T (2880 x 4096 bf16)
+    # gradient buffer (4096 x 12288 bf16), the block's h^T (2880 x 4096 bf16)
     # plus per-token state
-    fixed = 4096 * 16384 * 2 + 2880 * 4096 * 2
+    fixed = 4096 * 12288 * 2 + 2880 * 4096 * 2
     assert fixed <= n < fixed + 4096 * 8 * 1024
     # per-token growth is linear once T exceeds one block
     _, a = _ws(65536, 2880, 201088, 64)
@@ -132,17 +132,17 @@ def test_split_entry_point_sizes():
     assert code == 0
     code, fwd = _size(L.kd_topk_kl_fwd_workspace_size, T, H, V, K)
     assert code == 0
-    # the forward needs no gradient buffer (4096 x 16384 bf16), no h^T (2880 x 4096 bf16)
+    # the forward needs no gradient buffer (4096 x 12288 bf16), no h^T (2880 x 4096 bf16)
     # and no per-token pass-2 offsets (4096 fp32)
-    assert full - fwd == 4096 * 16384 * 2 + H * 4096 * 2 + 4 * 4096
+    assert full - fwd == 4096 * 12288 * 2 + H * 4096 * 2 + 4 * 4096
     code, saved = _size(L.kd_topk_kl_saved_size, T, H, V, K)
     assert code == 0
     # log-sum-exp [T] and the gathered logits [T, K], fp32, 256-byte aligned pieces
     assert 4 * T + 4 * T * K <= saved <= 4 * T + 4 * T * K + 1024
-    # bf16 gradient outputs stage fp32 dH [T, H] and one dW chunk [16384, H]
+    # bf16 gradient outputs stage fp32 dH [T, H] and one dW chunk [12288, H]
     code, b16 = _size(L.kd_topk_kl_workspace_size, T, H, V, K, flags=kd.KD_FLAG_GRAD_BF16)
     assert code == 0
-    assert b16 - full == 4 * T * H + 4 * 16384 * H
+    assert b16 - full == 4 * T * H + 4 * 12288 * H
     # accumulate flags change nothing in the plan; unknown flags are rejected
     assert _size(L.kd_topk_kl_workspace_size, T, H, V, K,
                  flags=kd.KD_FLAG_ACCUMULATE_DH | kd.KD_FLAG_ACCUMULATE_DW) == (0, full)
