@@ -148,10 +148,11 @@ def test_split_entry_point_sizes():
                  flags=kd.KD_FLAG_ACCUMULATE_DH | kd.KD_FLAG_ACCUMULATE_DW) == (0, full)
     assert _size(L.kd_topk_kl_workspace_size, T, H, V, K, flags=32)[0] == 1
     # the sequence-chunk schedule keeps one token block of fp32 logits (block 4096 by default)
+    # and defaults to vocabulary chunks of 16384 (12288 otherwise)
     code, sq = _size(L.kd_topk_kl_workspace_size, T, H, V, K, flags=kd.KD_FLAG_SEQ_CHUNK)
-    assert code == 0 and sq - full == 4 * V * 4096
-    assert _size(L.kd_topk_kl_workspace_size, T, H, V, K, flags=kd.KD_FLAG_SEQ_CHUNK, block_t=1024)[1] - \
-        _size(L.kd_topk_kl_workspace_size, T, H, V, K, block_t=1024)[1] == 4 * V * 1024
+    assert code == 0 and sq - full == 4 * V * 4096 + 4096 * (16384 - 12288) * 2
+    assert _size(L.kd_topk_kl_workspace_size, T, H, V, K, flags=kd.KD_FLAG_SEQ_CHUNK, block_t=1024,
+                 chunk_v=12288)[1] - _size(L.kd_topk_kl_workspace_size, T, H, V, K, block_t=1024)[1] == 4 * V * 1024
     for fn in (L.kd_topk_kl_saved_size, L.kd_topk_kl_fwd_workspace_size):
         assert _size(fn, T, 2900, V, K)[0] == 2
 
