@@ -6,14 +6,23 @@
 //
 // One 512-thread workgroup per row, values compared as 16-bit
 // order-preserving keys:
-//   1. one pass over the row keeps each thread's two largest keys; the K-th
-//      largest of those 1024 keys, theta, is a lower bound of the row's K-th
-//      largest (K distinct elements reach it), found bit by bit;
-//   2. a second pass appends every (key, id) with key >= theta to LDS (for
-//      ordinary rows a small multiple of K; the second read mostly hits the
-//      last-level cache);
+//   1. one pass over the row: each thread keeps the two largest keys of its
+//      even-indexed and of its odd-indexed elements, both pairs in the two
+//      16-bit halves of two registers (packed 16-bit min / max, about four
+//      ALU operations per element); theta, the K-th largest of those 2048
+//      keys, is a lower bound of the row's K-th largest (K distinct elements
+//      reach it), found bit by bit;
+//   2. every (key, id) with key >= theta goes to LDS: the pass also noted
+//      where each half's best key was seen, which is all a thread holds at or
+//      above theta unless its second key reaches theta too; only such
+//      threads' shares of the row (one in 512 vectors each) are scanned
+//      again, one share per wave with a vector per lane (for ordinary rows a
+//      few shares);
 //   3. the candidates are sorted in LDS (bitonic: descending key, ascending
 //      id) and the first K written out.
+// The pass ranks -0 just below +0 (raw keys); a theta at either zero is
+// lowered to the -0 key, so that every zero is a candidate, and the
+// candidates carry keys on which -0 equals +0.
 // Rows where more than kTopkCand keys reach theta (e.g. long runs of equal
 // values) take an exact slow path: the K-th largest key and the cut among
 // its ties are found bit by bit with a pass over the row per bit, then
@@ -31,6 +40,21 @@ constexpr int kTopkCand = 4096;
 __device__ __forceinline__ uint32_t bf16_key(uint32_t b) {
   b = (b == 0x8000u) ? 0u : b;
   return (b & 0x8000u) ? (~b & 0xFFFFu) : (b | 0x8000u);
+}
+// the raw order-preserving keys of a packed bf16 pair, both halves at once
+// (x ^ 0x8000 for a clear sign bit, ~x for a set one; -0 sits just below +0)
+__device__ __forceinline__ uint32_t raw_key2(uint32_t x) {
+  return x ^ (((x >> 15) & 0x00010001u) * 0x7FFFu + 0x80008000u);
+}
+__device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
+  typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t,
+                            __builtin_elementwise_max(__builtin_bit_cast(u16x2, a), __builtin_bit_cast(u16x2, b)));
+}
+__device__ __forceinline__ uint32_t pk_min_u16(uint32_t a, uint32_t b) {
+  typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t,
+                            __builtin_elementwise_min(__builtin_bit_cast(u16x2, a), __builtin_bit_cast(u16x2, b)));
 }
 __device__ __forceinline__ float key_bf16_value(uint32_t k) {
   const uint32_t b = (k & 0x8000u) ? (k & 0x7FFFu) : (~k & 0xFFFFu);
@@ -98,47 +122,95 @@ __global__ void __launch_bounds__(kTopkThreads) k_topk(TopkArgs a) {
   __shared__ uint32_t ck[kTopkCand];
   __shared__ int32_t ci[kTopkCand];
   __shared__ int red[2][kTopkThreads / 64];
-  __shared__ int ncand;
+  __shared__ int16_t shares[kTopkThreads];
+  __shared__ int ncand, nshares;
   const int tid = threadIdx.x;
   const int64_t t = blockIdx.x;
   const int64_t V = a.V, nvec = V >> 3;
   const int K = a.K;
   const uint16_t* row = a.X + t * V;
   int rb = 0;
-  // 1. each thread's two largest keys; theta = K-th largest of them
-  uint32_t m1 = 0, m2 = 0;
-  for (int64_t i = tid; i < nvec; i += kTopkThreads) {
-    uint32_t k[8];
-    load_keys(row, i, k);
+  // 1. per half (even / odd elements): m1 = largest raw key, m2 = second
+  uint32_t m1 = 0, m2 = 0;  // key 0 (the pattern 0xFFFF, a NaN) is the floor
+  // word of the thread's share (4 per vector) where each half's m1 was seen
+  int p_lo = 0, p_hi = 0;
+  constexpr int kAhead = 4;  // vectors in flight per thread
+  int pos = 0;
+  for (int64_t i0 = tid; i0 < nvec; i0 += (int64_t)kAhead * kTopkThreads) {
+    u32x4 v[kAhead];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const uint32_t lo = k[q] < m1 ? k[q] : m1;
-      m1 = k[q] > m1 ? k[q] : m1;
-      m2 = lo > m2 ? lo : m2;
+    for (int u = 0; u < kAhead; ++u) {
+      const int64_t i = i0 + (int64_t)u * kTopkThreads;
+      // past the row: the floor pattern, which changes no kept key
+      v[u] = i < nvec ? reinterpret_cast<const u32x4*>(row)[i] : u32x4{~0u, ~0u, ~0u, ~0u};
     }
+#pragma unroll
+    for (int u = 0; u < kAhead; ++u)
+#pragma unroll
+      for (int q = 0; q < 4; ++q, ++pos) {
+        const uint32_t k = raw_key2(v[u][q]);
+        const uint32_t lo = pk_min_u16(k, m1);
+        const uint32_t n1 = pk_max_u16(k, m1);
+        const uint32_t ch = n1 ^ m1;  // a half changes only for a strictly larger key
+        p_lo = (ch & 0xFFFFu) ? pos : p_lo;
+        p_hi = (ch >> 16) ? pos : p_hi;
+        m1 = n1;
+        m2 = pk_max_u16(lo, m2);
+      }
   }
-  if (tid == 0) ncand = 0;
+  if (tid == 0) {
+    ncand = 0;
+    nshares = 0;
+  }
   uint32_t theta = 0;
   for (int b = 15; b >= 0; --b) {
     const uint32_t cand = theta | (1u << b);
-    if (block_count((m1 >= cand) + (m2 >= cand), red[rb]) >= K) theta = cand;
+    const int n = ((m1 & 0xFFFFu) >= cand) + ((m1 >> 16) >= cand) + ((m2 & 0xFFFFu) >= cand) + ((m2 >> 16) >= cand);
+    if (block_count(n, red[rb]) >= K) theta = cand;
     rb ^= 1;
   }
-  // the elements behind the 1024 kept keys are distinct, so at least K keys
-  // of the row are >= theta
-  // 2. candidates: every key >= theta
-  for (int64_t i = tid; i < nvec; i += kTopkThreads) {
-    uint32_t k[8];
-    load_keys(row, i, k);
+  // the elements behind the 2048 kept keys are distinct, so at least K keys
+  // of the row are >= theta; at a zero theta both zeros become candidates
+  if (theta == 0x7FFFu || theta == 0x8000u) theta = 0x7FFFu;
+  // 2. candidates: every element with key >= theta.  A half whose second key
+  // is below theta holds at most its best element there (known with its
+  // position); a thread with a second key >= theta may have dropped some, and
+  // its share is scanned again
+  if ((m2 & 0xFFFFu) >= theta || (m2 >> 16) >= theta) {
+    shares[atomicAdd(&nshares, 1)] = (int16_t)tid;
+  } else {
 #pragma unroll
-    for (int q = 0; q < 8; ++q)
-      if (k[q] >= theta) {
+    for (int hf = 0; hf < 2; ++hf) {
+      const uint32_t rk = hf ? (m1 >> 16) : (m1 & 0xFFFFu);
+      if (rk >= theta) {
+        const int pw = hf ? p_hi : p_lo;
         const int p = atomicAdd(&ncand, 1);
         if (p < kTopkCand) {
-          ck[p] = k[q];
-          ci[p] = (int32_t)(8 * i + q);
+          ck[p] = rk == 0x7FFFu ? 0x8000u : rk;  // -0 as +0
+          ci[p] = (int32_t)(8 * ((int64_t)tid + (int64_t)kTopkThreads * (pw >> 2)) + 2 * (pw & 3) + hf);
         }
       }
+    }
+  }
+  __syncthreads();
+  {
+    const int lane = tid & 63, nsh = nshares;
+    for (int sh = tid >> 6; sh < nsh; sh += kTopkThreads / 64) {
+      const int64_t r = shares[sh];
+      for (int64_t i = r + (int64_t)kTopkThreads * lane; i < nvec; i += (int64_t)kTopkThreads * 64) {
+        uint32_t k[8];
+        load_keys(row, i, k);  // keys with -0 == +0: the same test against theta
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+          if (k[q] >= theta) {
+            const int p = atomicAdd(&ncand, 1);
+            if (p < kTopkCand) {
+              ck[p] = k[q];
+              ci[p] = (int32_t)(8 * i + q);
+            }
+          }
+      }
+    }
   }
   __syncthreads();
   const int nc = ncand;

@@ -195,7 +195,8 @@ kd_status kd_topk_kl_logits(const kd_logits_problem* p, const void* Z,
  * largest values in descending order of value, equal values by ascending id
  * (so the result is unique; -0 counts as +0), and the values (exact, fp32).
  * Values are ordered as real numbers; NaN rows are a precondition violation.
- * v1 limits: V % 8 == 0 (KD_ERR_UNSUPPORTED otherwise), 1 <= K <= min(V, 1024).
+ * v1 limits: V % 8 == 0 and V <= 2^30 - 1 (KD_ERR_UNSUPPORTED otherwise),
+ * 1 <= K <= min(V, 1024).
  * No workspace; asynchronous on `stream`.
  */
 typedef struct kd_topk_problem {

@@ -177,3 +177,22 @@ def test_split_entry_points_reject_bad_arguments_before_any_hip_call():
                             fake, big, vp(0)) == 2
     assert L.kd_topk_kl_bwd(ctypes.byref(p), fake, fake, fake, fake, vp(0), fake, vp(0), fake, vp(0), fake,
                             ctypes.c_size_t(8), vp(0)) == 3
+
+
+def test_topk_select_validates_before_any_hip_call():
+    L = kd.lib()
+    vp = ctypes.c_void_p
+    fake = vp(1 << 20)  # never dereferenced: validation fails first
+
+    def call(T, V, K, flags=0, X=fake):
+        p = kd.KdTopkProblem(T, V, K, flags)
+        return L.kd_topk_select(ctypes.byref(p), X, fake, fake, vp(0))
+
+    assert call(4, 1000, 0) == 1               # K = 0
+    assert call(4, 1000, 2000) == 1            # K > V
+    assert call(4, 1000, 4, flags=1) == 1      # unknown flag
+    assert call(4, 1000, 4, X=vp(0)) == 1      # null input
+    assert call(4, 1001, 4) == 2               # V % 8
+    assert call(4, 2048, 1025) == 2            # K > 1024
+    assert call(4, 1 << 30, 4) == 2            # V past 2^30 - 1
+    assert call(4, 1000, 4, X=vp((1 << 20) + 2)) == 2  # misaligned rows

@@ -56,6 +56,23 @@ def test_teacher_rows_at_the_gpt_oss_vocabulary():
     check(X, 100)
 
 
+def test_top_values_crowded_into_one_threads_share():
+    """A row's 512 threads each keep their two best elements from one pass;
+    a thread holding more of the top K (here all of them, or pairs of equal
+    values) must rescan its share.  Thread r's share is vectors r, r + 512, ...
+    of 8 values each."""
+    r = np.random.default_rng(4)
+    V = 201088
+    X = (r.standard_normal((6, V)) * 2).astype(np.float32)
+    share = lambda tid, n: (8 * (tid + 512 * np.arange(n))[:, None] + np.arange(8)[None, :]).ravel()
+    X[0, share(5, 16)[:128]] = 50.0 + np.arange(128)          # top 128 all in thread 5
+    X[1, share(9, 8)[:64]] = 40.0                              # 64 equal maxima in thread 9
+    X[2, share(0, 49)[-8:]] = 30.0                             # at the end of thread 0's share
+    X[3, share(511, 4)] = 20.0 + np.arange(32) % 3             # ties inside one thread
+    check(X, 64)
+    check(X, 100)
+
+
 def test_unsupported_shapes_are_rejected():
     X = torch.zeros(4, 1001, dtype=torch.bfloat16, device="cuda")
     with pytest.raises(kd.KdError) as e:
