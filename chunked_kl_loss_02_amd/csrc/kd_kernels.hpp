@@ -664,9 +664,24 @@ __global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 
     nvalid = a.vrows;
     acc_mode = a.acc_dw;
   }
+  // Accumulating: the 16 old values of a token/vocabulary column are read
+  // with unconditional buffer loads before any is used (one wait per column,
+  // not one per value).  Past the output rows the range check reads zeros;
+  // past H within a row the values are not stored.
+  const __amdgpu_buffer_rsrc_t ro = make_rsrc(out, (uint64_t)nvalid * (uint64_t)a.H * 4u);
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int64_t n = (int64_t)nt * 256 + wn * 128 + acc_col(j, lane);
+    f32x4 old[4][4];
+    if (acc_mode) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int64_t m = (int64_t)mt * 256 + wm * 128 + acc_row(i, 4 * q, lane);
+          old[i][q] = __builtin_bit_cast(f32x4, buf_load16(ro, (uint32_t)((n * a.H + m) * 4)));
+        }
+    }
     if (n >= nvalid) continue;
     float* orow = out + n * a.H;
 #pragma unroll
@@ -676,9 +691,8 @@ __global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 
         const int64_t m = (int64_t)mt * 256 + wm * 128 + acc_row(i, 4 * q, lane);
         if (m >= a.H) continue;
         f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-        f32x4* dst = reinterpret_cast<f32x4*>(orow + m);
-        if (acc_mode) v += *dst;
-        *dst = v;
+        if (acc_mode) v += old[i][q];
+        *reinterpret_cast<f32x4*>(orow + m) = v;
       }
   }
 }
