@@ -14,9 +14,15 @@
 
 namespace {
 
+// Default tiling (measured at H = 2880, V = 201088): token blocks of 8192;
+// vocabulary chunks of 12288 for a block of at most 4096 tokens, else 8192,
+// so the bf16 gradient buffer (block x chunk) stays near 100-130 MB and, with
+// the chunk's W rows, inside the last-level cache; the sequence-chunk
+// schedule keeps blocks of 4096 and chunks of 16384.
 constexpr int kDefaultChunkV = 12288;
-constexpr int kDefaultSeqChunkV = 16384;  // measured best for the sequence-chunk schedule
-constexpr int kDefaultBlockT = 16384;
+constexpr int kDefaultChunkVLargeBlock = 8192;
+constexpr int kDefaultSeqChunkV = 16384;
+constexpr int kDefaultBlockT = 8192;
 constexpr int kDefaultSeqBlockT = 4096;
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -66,8 +72,8 @@ kd_status check(const kd_problem* p) {
   if (p->K > kd::kTeacherMaxK) return KD_ERR_UNSUPPORTED;
   if (p->chunk_v % 256 != 0 || p->block_t % 256 != 0) return KD_ERR_UNSUPPORTED;
   if (p->V > (int64_t)INT32_MAX || p->T > ((int64_t)1 << 40)) return KD_ERR_UNSUPPORTED;
-  const int64_t cv = p->chunk_v ? p->chunk_v : std::max(kDefaultChunkV, kDefaultSeqChunkV);
-  const int64_t bt = p->block_t ? p->block_t : kDefaultBlockT;
+  const int64_t cv = p->chunk_v ? p->chunk_v : std::max(kDefaultChunkV, kDefaultSeqChunkV);  // largest default
+  const int64_t bt = p->block_t ? p->block_t : std::max(kDefaultBlockT, kDefaultSeqBlockT);
   // 32-bit buffer offsets inside one chunk / block operand
   const int64_t lim = (int64_t)UINT32_MAX;
   if (cv * p->H * 2 > lim || bt * p->H * 2 > lim || bt * cv * 2 > lim) return KD_ERR_UNSUPPORTED;
@@ -85,10 +91,13 @@ Plan make_plan(const kd_problem* p, bool with_grad = true) {
   P.K = p->K;
   P.tau = p->tau;
   P.seq = with_grad && (p->flags & KD_FLAG_SEQ_CHUNK);
-  P.chunk_v = p->chunk_v ? p->chunk_v : P.seq ? kDefaultSeqChunkV : kDefaultChunkV;
   P.block_t = p->block_t ? p->block_t : P.seq ? kDefaultSeqBlockT : kDefaultBlockT;
   P.Tb = P.T < P.block_t ? align256(P.T) : P.block_t;
   if (P.Tb == 0) P.Tb = 256;
+  P.chunk_v = p->chunk_v              ? p->chunk_v
+              : P.seq                 ? kDefaultSeqChunkV
+              : P.Tb <= 4096          ? kDefaultChunkV
+                                      : kDefaultChunkVLargeBlock;
   P.ntt_max = (int)(P.Tb / 256);
   P.nvt = cdiv(P.V, 256);
   P.nranges = (int)P.nvt;

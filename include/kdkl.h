@@ -80,9 +80,11 @@ typedef struct kd_problem {
   int64_t V;        /* vocabulary size; >= 1 */
   int32_t K;        /* cached teacher entries per token; 1 <= K <= min(V, 1024) */
   float tau;        /* temperature; finite, > 0 */
-  int32_t chunk_v;  /* vocabulary chunk of the gradient pass; 0 = 12288 (16384 with
-                       KD_FLAG_SEQ_CHUNK); multiple of 256 */
-  int32_t block_t;  /* token block of both passes; 0 = 16384; multiple of 256 */
+  int32_t chunk_v;  /* vocabulary chunk of the gradient pass, multiple of 256;
+                       0 = 12288 for a token block of at most 4096, else 8192
+                       (16384 with KD_FLAG_SEQ_CHUNK) */
+  int32_t block_t;  /* token block of both passes, multiple of 256; 0 = 8192
+                       (4096 with KD_FLAG_SEQ_CHUNK) */
   uint32_t flags;   /* KD_FLAG_* */
 } kd_problem;
 

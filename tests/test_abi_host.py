@@ -196,3 +196,17 @@ def test_topk_select_validates_before_any_hip_call():
     assert call(4, 2048, 1025) == 2            # K > 1024
     assert call(4, 1 << 30, 4) == 2            # V past 2^30 - 1
     assert call(4, 1000, 4, X=vp((1 << 20) + 2)) == 2  # misaligned rows
+
+
+def test_default_tiling():
+    """Defaults: token blocks of 8192 (4096 for the sequence-chunk schedule),
+    vocabulary chunks of 12288 while a block holds at most 4096 tokens, else
+    8192 (16384 for the sequence-chunk schedule)."""
+    H, V, K = 2880, 201088, 64
+    for T, cv, bt in [(4096, 12288, 8192), (3000, 12288, 8192), (6000, 8192, 8192), (65536, 8192, 8192)]:
+        assert _ws(T, H, V, K)[1] == _ws(T, H, V, K, chunk_v=cv, block_t=bt)[1], T
+    assert _ws(65536, H, V, K)[1] != _ws(65536, H, V, K, chunk_v=12288, block_t=16384)[1]
+    L = kd.lib()
+    seq = kd.KD_FLAG_SEQ_CHUNK
+    assert _size(L.kd_topk_kl_workspace_size, 65536, H, V, K, flags=seq)[1] == \
+        _size(L.kd_topk_kl_workspace_size, 65536, H, V, K, flags=seq, chunk_v=16384, block_t=4096)[1]

@@ -144,7 +144,7 @@ def test_peak_memory_linear_in_tokens():
     linearly in T with a per-token slope far below the 2V bytes of one bf16
     logit row."""
     H, V, K = 2880, 201088, 64
-    Ts = [16384, 32768, 65536, 131072]  # at and above one token block: fixed workspace
+    Ts = [16384, 32768, 65536, 131072]  # above one token block (8192): fixed workspace
     peaks = []
     for T in Ts:
         x = synth.make_inputs_torch(T, H, V, K, seed=1)
