@@ -664,36 +664,59 @@ __global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 
     nvalid = a.vrows;
     acc_mode = a.acc_dw;
   }
-  // Accumulating: the 16 old values of a token/vocabulary column are read
-  // with unconditional buffer loads before any is used (one wait per column,
-  // not one per value).  Past the output rows the range check reads zeros;
-  // past H within a row the values are not stored.
-  const __amdgpu_buffer_rsrc_t ro = make_rsrc(out, (uint64_t)nvalid * (uint64_t)a.H * 4u);
+  // The wave's 128 (m) x 128 (n) block leaves through a private 32 KiB LDS
+  // stage (free after gemm_tile), 64 columns n at a time: each lane writes its
+  // 4 consecutive m of one n (16-byte chunk m/4 of row n stored at position
+  // (m/4) ^ (n & 31), so the 32 columns of one write land in different
+  // banks), then every row n leaves as one 512-byte segment (32 lanes x 16
+  // bytes) instead of 32-byte pieces of 32 rows per store.  Accumulating
+  // reads the old values the same coalesced way (range-checked: zeros past
+  // the output's rows; past H within a row they are not stored).
+  {
+    const int w = threadIdx.x >> 6;
+    float* stg = reinterpret_cast<float*>(w == 0 ? st.a0 : w == 1 ? st.a1 : w == 2 ? st.b0 : st.b1);
+    const int64_t m0 = (int64_t)mt * 256 + wm * 128;  // the wave's first m
+    const int64_t n0 = (int64_t)nt * 256 + wn * 128;  // the wave's first n
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc(out, (uint64_t)nvalid * (uint64_t)a.H * 4u);
+    const int c = lane & 31;              // 16-byte chunk of a row: m = m0 + 4c .. 4c+3
+    const bool m_ok = m0 + 4 * c < a.H;   // H % 64 == 0: a chunk is all in or all out
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int64_t n = (int64_t)nt * 256 + wn * 128 + acc_col(j, lane);
-    f32x4 old[4][4];
-    if (acc_mode) {
+    for (int half = 0; half < 2; ++half) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int jj = 0; jj < 2; ++jj) {
+        const int j = 2 * half + jj;
+        const int nl = 32 * jj + (lane & 31);  // row of the stage
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int64_t m = (int64_t)mt * 256 + wm * 128 + acc_row(i, 4 * q, lane);
-          old[i][q] = __builtin_bit_cast(f32x4, buf_load16(ro, (uint32_t)((n * a.H + m) * 4)));
-        }
-    }
-    if (n >= nvalid) continue;
-    float* orow = out + n * a.H;
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int64_t m = (int64_t)mt * 256 + wm * 128 + acc_row(i, 4 * q, lane);
-        if (m >= a.H) continue;
-        f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-        if (acc_mode) v += old[i][q];
-        *reinterpret_cast<f32x4*>(orow + m) = v;
+          for (int q = 0; q < 4; ++q) {
+            const int ml = acc_row(i, 4 * q, lane);  // 4-aligned m within the wave's block
+            const f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+            *reinterpret_cast<f32x4*>(stg + nl * 128 + (((ml >> 2) ^ (nl & 31)) << 2)) = v;
+          }
       }
+      __builtin_amdgcn_wave_barrier();
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      // rows r = 2k + (lane >> 5) of this half, k = 0..31
+      f32x4 old[32];
+      if (acc_mode) {
+#pragma unroll
+        for (int k = 0; k < 32; ++k) {
+          const int64_t n = n0 + 64 * half + 2 * k + (lane >> 5);
+          old[k] = __builtin_bit_cast(f32x4, buf_load16(ro, (uint32_t)((n * a.H + m0 + 4 * c) * 4)));
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < 32; ++k) {
+        const int nl = 2 * k + (lane >> 5);
+        const int64_t n = n0 + 64 * half + nl;
+        f32x4 v = *reinterpret_cast<const f32x4*>(stg + nl * 128 + ((c ^ (nl & 31)) << 2));
+        if (acc_mode) v += old[k];
+        if (n < nvalid && m_ok) *reinterpret_cast<f32x4*>(out + n * a.H + m0 + 4 * c) = v;
+      }
+      __builtin_amdgcn_wave_barrier();
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    }
   }
 }
 
