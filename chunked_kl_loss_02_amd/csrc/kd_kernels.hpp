@@ -8,17 +8,19 @@
 // cached top-K logits, renormalised over those K entries; the backward pass
 // recomputes each block.  With c = log2(e)/tau all exponentials run in base 2.
 //
-//   pass 1 : k_pass1   S^T tile = W_tile h_tile^T (MFMA), per token running
-//                      (max, sum 2^(c S - max)) over its vocabulary range
-//            k_lse     merges the per-range partials -> lse2[t] (log2 units)
+//   pass 1 : k_pass1   S^T tile = W_tile h_tile^T (MFMA), per token the
+//                      tile's (max, sum 2^(c S - max))
+//            k_lse     merges the per-tile partials -> lse2[t] (log2 units)
 //   teacher: k_teacher p = softmax_K(u/tau), merged mass of duplicate ids,
 //                      sum_k p log(mass) per row; k_gather s[t,k] = S[t, idx]
 //   loss   : k_rows / k_sum   KL_t = sum p log p - sum p s / tau + LSE_t
 //   pass 2 : k_pass2   recomputes the S^T tile, writes the logit gradient
 //                      G = coef * 2^(c S - lse2) (bf16) for one (token block,
-//                      vocabulary chunk); k_fixup subtracts the teacher mass
-//                      at the cached ids; k_bwd contracts G into dH (over the
-//                      chunk's vocabulary) and dW (over the block's tokens).
+//                      vocabulary chunk), with the per-token offsets of
+//                      k_offsets; k_fixup subtracts the teacher mass at the
+//                      cached ids; k_bwd contracts G into dH (over the chunk's
+//                      vocabulary) and dW (over the block's tokens, with h^T
+//                      from k_transpose_h).
 #pragma once
 #include "kd_gemm.hpp"
 
@@ -178,10 +180,10 @@ __global__ void __launch_bounds__(256) k_gather(const uint16_t* __restrict__ h, 
 }
 
 // ----------------------------------------------------------------- pass 1
-// Grid: padded to a multiple of 8; work id -> (token tile, vocabulary range).
-// Each workgroup walks `per` vocabulary tiles of 256 for one token tile of
-// 256 and writes one (max, sum) pair per token for its range:
-//   part[range * ldp + t] = (m, l) with l = sum_v 2^(c S[t,v] - m).
+// Grid: padded to a multiple of 8; work id -> (token tile, vocabulary tile),
+// both of 256.  Each workgroup writes one (max, sum) pair per token of its
+// tile:  part[vt * ldp + t] = (m, l) with l = sum_v 2^(c S[t,v] - m) over the
+// tile's vocabulary rows.
 struct Pass1Args {
   const uint16_t* W;     // [V, H]
   const uint16_t* h;     // token block origin [rows, H]
@@ -316,7 +318,7 @@ __global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 
 }
 
 // lse2[t] = log2 sum_v 2^(c S[t,v]) from the per-tile partials.  A block
-// handles 32 tokens; its 8 thread groups each fold every 8th range, then the
+// handles 32 tokens; its 8 thread groups each fold every 8th tile, then the
 // 8 partial results are folded in a fixed order (deterministic).
 __global__ void __launch_bounds__(256) k_lse(const float2* __restrict__ part, int nranges, int ldp, int64_t rows,
                                              float* __restrict__ lse2) {
