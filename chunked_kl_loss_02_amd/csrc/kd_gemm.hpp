@@ -4,10 +4,11 @@
 // owns a (32*MI) x (32*NI) block of the output tile, held in MI*NI
 // v_mfma_f32_32x32x16_bf16 accumulators (16 fp32 per lane each).  K advances
 // 64 at a time (four MFMA sub-steps of 16) through two LDS stages per
-// operand; the loads of step k+1 are in flight while the MFMAs of step k run,
-// so one barrier per step suffices.  That barrier sits between sub-steps 2
-// and 3: sub-step 3's fragments are already in registers, so its MFMAs cover
-// the fetch of the next stage's first fragments after the barrier.
+// operand, with one barrier per step between sub-steps 2 and 3: sub-step 3's
+// fragments are already in registers by then, so its MFMAs cover the fetch
+// of the next stage's first fragments after the barrier.  The barrier also
+// frees the stage just consumed, and the loads of the step after next go
+// into it right away, so global data has a full step of MFMAs to arrive.
 //
 // Operands are loaded with raw buffer loads whose range ends exactly at the
 // last valid row: out-of-range rows read as zero, which covers the ragged
@@ -20,14 +21,13 @@
 // swz does not depend on bits >= 5 of r, so the fragment reads of the 32-row
 // subtiles of a wave differ only by an immediate offset.  The four stages
 // (A0, A1, B0, B1) are distinct LDS objects so the compiler may move the
-// loads into stage k+1 across the fragment reads of stage k.
+// loads into one stage across the fragment reads of the other.
 //
-// Two operand layouts are supported:
+// Two operand layouts are supported, both loaded global -> LDS directly
+// (buffer_load_dwordx4 ... lds):
 //   KC : element (row, k) at base + row*ld + k   (k contiguous; e.g. W, h for S = W h^T)
-//   RC : element (row, k) at base + k*ld + row   (row contiguous; e.g. W in dH = G W)
-// KC tiles go global -> LDS directly (buffer_load_dwordx4 ... lds); RC tiles
-// are loaded as 8x8 bf16 blocks into registers, transposed with v_perm_b32
-// and written to LDS, so the MFMAs always read k-contiguous rows.
+//   TR : element (row, k) at base + k*ld + row   (row contiguous; e.g. W in dH = G W),
+//        read out of LDS with transposing fragment reads.
 #pragma once
 #include "kd_common.hpp"
 
@@ -51,7 +51,6 @@ template <int R>
 struct LoaderKC {
   static constexpr int NQ = R / 32;  // wave instructions per wave per k-step
   static constexpr int kVmem = NQ;   // vector-memory instructions per k-step
-  static constexpr int kDsw = 0;     // LDS write instructions per k-step
   static constexpr int kReads = 1;   // LDS read instructions per MFMA fragment
   __amdgpu_buffer_rsrc_t rs;
   uint32_t voff[NQ];
@@ -79,8 +78,6 @@ struct LoaderKC {
                                                __builtin_amdgcn_readfirstlane(kt * (kBK * 2)), 0, 0);
     }
   }
-  __device__ __forceinline__ void load(int) {}
-  __device__ __forceinline__ void store(uint16_t*) const {}
   // MFMA fragment of sub-step s: row rbase + lane % 32, k = 16 s + 8 (lane / 32) + 0..7
   static __device__ __forceinline__ bf16x8 frag(const uint16_t* st, int rbase, int s, int lane) {
     return __builtin_bit_cast(bf16x8,
@@ -100,7 +97,6 @@ struct LoaderKC {
 struct LoaderTR {
   static constexpr int NQ = 8;       // 64 rows x 512 B = 32 KiB = 8 x 1 KiB per wave
   static constexpr int kVmem = NQ;
-  static constexpr int kDsw = 0;
   static constexpr int kReads = 2;
   __amdgpu_buffer_rsrc_t rs;
   uint32_t voff[NQ];
@@ -134,8 +130,6 @@ struct LoaderTR {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)dst, 16, voff[j] + o, 0, 0, 0);
     }
   }
-  __device__ __forceinline__ void load(int) {}
-  __device__ __forceinline__ void store(uint16_t*) const {}
   static __device__ __forceinline__ bf16x8 frag(const uint16_t* st, int rbase, int s, int lane) {
     typedef short v4i16 __attribute__((ext_vector_type(4)));
     const int g = lane >> 4, i = lane & 15;
@@ -152,57 +146,6 @@ struct LoaderTR {
     const short __attribute__((ext_vector_type(8))) x = {v[0][0], v[0][1], v[0][2], v[0][3],
                                                          v[1][0], v[1][1], v[1][2], v[1][3]};
     return __builtin_bit_cast(bf16x8, x);
-  }
-};
-
-// Loader for a tile of R rows x 64 k of a row-contiguous operand (transposed
-// in registers).  R must be a multiple of 8 and R/8 * 8 <= 256 threads.
-template <int R>
-struct LoaderRC {
-  static constexpr int NB = R / 8;  // 8-row blocks across the tile
-  static constexpr int kVmem = 8;
-  static constexpr int kDsw = 8;
-  static constexpr int kReads = 1;
-  u32x4 v[8];
-  __amdgpu_buffer_rsrc_t rs;
-  uint32_t off0;
-  uint32_t ldb;
-  int mb, kb;
-  bool active;
-
-  // base: address of (row 0, k = 0) of the operand's k-origin; rows are the
-  // contiguous dimension; row0: first row of the tile; k_left: valid k rows.
-  __device__ __forceinline__ void init(const uint16_t* base, int64_t k_left, int64_t ld, int row0) {
-    const int tid = threadIdx.x;
-    ldb = (uint32_t)(ld * 2);
-    rs = make_rsrc(base, k_left > 0 ? (uint64_t)k_left * (uint64_t)ldb : 0);
-    mb = tid % NB;
-    kb = tid / NB;
-    active = kb < 8;
-    off0 = (uint32_t)(kb * 8) * ldb + (uint32_t)(row0 + mb * 8) * 2u;
-  }
-  __device__ __forceinline__ void issue(int, uint16_t*) const {}
-  __device__ __forceinline__ void load(int kt) {
-    if (NB * 8 < kThreads && !active) return;
-    const uint32_t o = off0 + (uint32_t)kt * (uint32_t)kBK * ldb;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] = buf_load16(rs, o + (uint32_t)j * ldb);
-  }
-  __device__ __forceinline__ void store(uint16_t* s) const {
-    if (NB * 8 < kThreads && !active) return;
-    // v[kk].d[q] holds elements (2q, 2q+1) of k-row kk.  Output row mm holds
-    // k = 0..7 of column mm: dword p = (elem mm of k-row 2p, elem mm of 2p+1).
-#pragma unroll
-    for (int mm = 0; mm < 8; ++mm) {
-      const uint32_t sel = (mm & 1) ? 0x07060302u : 0x05040100u;
-      u32x4 y;
-#pragma unroll
-      for (int p = 0; p < 4; ++p) y[p] = __builtin_amdgcn_perm(v[2 * p + 1][mm >> 1], v[2 * p][mm >> 1], sel);
-      *reinterpret_cast<u32x4*>(s + lds_off(mb * 8 + mm, kb)) = y;
-    }
-  }
-  static __device__ __forceinline__ bf16x8 frag(const uint16_t* st, int rbase, int s, int lane) {
-    return LoaderKC<R>::frag(st, rbase, s, lane);
   }
 };
 
@@ -246,63 +189,49 @@ __device__ __forceinline__ void sched_substep() {
 __device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 __device__ __forceinline__ void wait_all() { asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory"); }
 
-// One k-step over stage (ca, cb) while step kn streams into (na, nb).
-//   region 1: the loads of step kn, sub-steps 0..2 (their MFMAs interleaved
-//             with the fragment reads of sub-steps 1..3 and the loads),
-//             register-staged LDS writes, then wait for this wave's loads
-//             and LDS traffic and meet the other waves;
-//   region 2: the first fragments of (na, nb) load under sub-step 3's MFMAs,
-//             whose fragments are already in registers, so the barrier's
-//             bubble is short.
+// One k-step over stage (ca, cb), whose successor (na, nb) is already in
+// flight:
+//   region 1: sub-steps 0..2, their MFMAs interleaved with the fragment reads
+//             of sub-steps 1..3; then wait for this wave's loads into (na, nb)
+//             and its LDS reads, and meet the other waves;
+//   region 2: (ca, cb) is free: the loads of step kn go into it, and the
+//             first fragments of (na, nb) load, under sub-step 3's MFMAs
+//             (their fragments are already in registers).
 // On entry a[0], b[0] hold sub-step 0 of (ca, cb); on exit of (na, nb).
-#ifndef KD_VMEM_SPREAD
-#define KD_VMEM_SPREAD 1
-#endif
-constexpr int kVmemSpread = KD_VMEM_SPREAD;
-
 template <int MI, int NI, class LA, class LB>
-__device__ __forceinline__ void kstep(LA& la, LB& lb, int kn, const uint16_t* ca, const uint16_t* cb, uint16_t* na,
-                                      uint16_t* nb, f32x16 (&acc)[MI][NI], bf16x8 (&a)[2][MI], bf16x8 (&b)[2][NI],
-                                      int arow0, int brow0, int lane) {
+__device__ __forceinline__ void kstep(LA& la, LB& lb, int kn, uint16_t* ca, uint16_t* cb, const uint16_t* na,
+                                      const uint16_t* nb, f32x16 (&acc)[MI][NI], bf16x8 (&a)[2][MI],
+                                      bf16x8 (&b)[2][NI], int arow0, int brow0, int lane) {
   constexpr int NM = MI * NI, NR = MI * LA::kReads + NI * LB::kReads;
-  constexpr int NVM = LA::kVmem + LB::kVmem, NDSW = LA::kDsw + LB::kDsw;
+  constexpr int NVM = LA::kVmem + LB::kVmem;
   static_assert(NR <= NM, "more fragment reads than MFMAs in a sub-step");
-  // the next stage's loads spread over the first kVmemSpread sub-steps
-  constexpr int per = (NVM + kVmemSpread - 1) / kVmemSpread;
-  constexpr int V0 = NVM < per ? NVM : per;
-  constexpr int V1 = (NVM - V0) < per ? (NVM - V0) : per;
-  constexpr int V2 = NVM - V0 - V1;
-  static_assert(V2 <= NM, "too many loads for one k-step");
-  la.issue(kn, na);
-  lb.issue(kn, nb);
-  la.load(kn);
-  lb.load(kn);
+  static_assert(NVM <= NM, "more loads than MFMAs in a sub-step");
 #pragma unroll
   for (int s = 0; s < 3; ++s) {
     load_frags<MI, NI, LA, LB>(ca, cb, a[(s + 1) & 1], b[(s + 1) & 1], arow0, brow0, lane, s + 1);
     mfma_substep<MI, NI>(acc, a[s & 1], b[s & 1]);
   }
-  la.store(na);
-  lb.store(nb);
-  sched_substep<NM, NR, V0>();
-  sched_substep<NM, NR, V1>();
-  sched_substep<NM, NR, V2>();
-  if constexpr (NDSW > 0) __builtin_amdgcn_sched_group_barrier(0x200, NDSW, 0);
+  sched_substep<NM, NR, 0>();
+  sched_substep<NM, NR, 0>();
+  sched_substep<NM, NR, 0>();
   wait_all();
   __syncthreads();
+  la.issue(kn, ca);
+  lb.issue(kn, cb);
   load_frags<MI, NI, LA, LB>(na, nb, a[0], b[0], arow0, brow0, lane, 0);
   mfma_substep<MI, NI>(acc, a[1], b[1]);
-  sched_substep<NM, NR, 0>();
+  sched_substep<NM, NR, NVM>();
 }
 
 // Full K loop for one output tile: acc = A_tile * B_tile^T over nk steps,
-// ping-ponging between the stage pairs (a0, b0) and (a1, b1).  Ends with
+// alternating between the stage pairs (a0, b0) and (a1, b1).  Ends with
 // every wave past a barrier that follows its last reads of the stages, so
 // the LDS can be reused (or the next tile started) right after.  The last
-// step re-fetches itself into the idle stage (never consumed), which keeps
-// every step identical.
+// two steps re-fetch step nk - 1 into the stage they free (never consumed),
+// which keeps every step identical.
 template <int MI, int NI, class LA, class LB>
 __device__ __forceinline__ void gemm_tile(LA& la, LB& lb, int nk, const Stages& st, f32x16 (&acc)[MI][NI]) {
+  constexpr int NVM = LA::kVmem + LB::kVmem;
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int arow0 = (w & 1) * 32 * MI;
@@ -320,19 +249,19 @@ __device__ __forceinline__ void gemm_tile(LA& la, LB& lb, int nk, const Stages& 
   uint16_t* sb = odd ? st.b1 : st.b0;
   la.issue(0, sa);
   lb.issue(0, sb);
-  la.load(0);
-  lb.load(0);
-  la.store(sa);
-  lb.store(sb);
-  wait_all();
+  la.issue(nk > 1 ? 1 : 0, odd ? st.a0 : st.a1);
+  lb.issue(nk > 1 ? 1 : 0, odd ? st.b0 : st.b1);
+  // step 0 has landed once at most step 1's loads are outstanding
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(NVM) : "memory");
   __syncthreads();
   load_frags<MI, NI, LA, LB>(sa, sb, a[0], b[0], arow0, brow0, lane, 0);
-  for (int kt = odd ? -1 : 0; kt + 1 < nk; kt += 2) {
-    if (kt >= 0) kstep<MI, NI>(la, lb, kt + 1, st.a0, st.b0, st.a1, st.b1, acc, a, b, arow0, brow0, lane);
-    kstep<MI, NI>(la, lb, kt + 2 < nk ? kt + 2 : kt + 1, st.a1, st.b1, st.a0, st.b0, acc, a, b, arow0, brow0, lane);
+  const int last = nk - 1;
+  for (int kt = odd ? -1 : 0; kt < last; kt += 2) {
+    if (kt >= 0) kstep<MI, NI>(la, lb, kt + 2 < nk ? kt + 2 : last, st.a0, st.b0, st.a1, st.b1, acc, a, b, arow0, brow0, lane);
+    kstep<MI, NI>(la, lb, kt + 3 < nk ? kt + 3 : last, st.a1, st.b1, st.a0, st.b0, acc, a, b, arow0, brow0, lane);
   }
-  // the last region read the idle stage's first fragments: let every wave
-  // finish its LDS reads before anyone reuses the stages
+  // the last region read the idle stage's first fragments and loaded into the
+  // stage it freed: let every wave finish both before anyone reuses the stages
   wait_all();
   __syncthreads();
 }
