@@ -266,32 +266,47 @@ __global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 
   // vocabulary rows of this lane: vt*256 + wm*128 + acc_row(i, e)
   const int64_t vbase = (int64_t)vt * 256 + wm * 128;
   if constexpr (kStore) store_tile_t(a, st, acc, vt, tt, wm, wn, lane);
-  if (vbase + 128 > a.V) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int e = 0; e < 16; ++e)
-        if (vbase + acc_row(i, e, lane) >= a.V)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) acc[i][j][e] = -INFINITY;
-  }
   float rm[4], rl[4];
+  if (vbase + 128 <= a.V) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    float mx = -INFINITY;
+    for (int j = 0; j < 4; ++j) {
+      float mx = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, acc[i][j][e]);
-    const float m = mx * a.c;
-    const float ref = m == -INFINITY ? 0.f : m;  // rows of this lane all past V
-    float sum = 0.f;
+        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, acc[i][j][e]);
+      const float m = mx * a.c;
+      float sum = 0.f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) sum += fast_exp2(fmaf(acc[i][j][e], a.c, -ref));
-    rm[j] = m;
-    rl[j] = sum;
+        for (int e = 0; e < 16; ++e) sum += fast_exp2(fmaf(acc[i][j][e], a.c, -m));
+      rm[j] = m;
+      rl[j] = sum;
+    }
+  } else {
+    // the vocabulary's last tile: rows of this wave at or past V count as
+    // absent (row r of the wave's block is valid iff r < lim)
+    const int lim = (int)(a.V - vbase);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          if (acc_row(i, e, lane) < lim) mx = fmaxf(mx, acc[i][j][e]);
+      const float m = mx * a.c;
+      const float ref = m == -INFINITY ? 0.f : m;  // rows of this lane all past V
+      float sum = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          if (acc_row(i, e, lane) < lim) sum += fast_exp2(fmaf(acc[i][j][e], a.c, -ref));
+      rm[j] = m;
+      rl[j] = sum;
+    }
   }
   // merge the two lane halves (same token, other vocabulary rows)
 #pragma unroll
