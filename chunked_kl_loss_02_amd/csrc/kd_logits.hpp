@@ -182,6 +182,9 @@ __global__ void __launch_bounds__(kLrowThreads) k_lrow(LrowArgs a) {
 // chunk c of thread i = vector c * 512 + i), so the row is read from HBM
 // once and dZ written once: 4 bytes per logit.
 constexpr int kLrowRegThreads = 512;
+// cache policy of the row's streaming loads and stores: nontemporal (each
+// byte of Z and dZ moves once)
+constexpr int kNT = 2;
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 
 template <int PER>
@@ -217,7 +220,7 @@ __global__ void __launch_bounds__(kLrowRegThreads) k_lrow_reg(LrowArgs a) {
       for (int c = 0; c < PER; ++c)
         if (in_row(c))
           __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, u32x4{0u, 0u, 0u, 0u}), rd, voff,
-                                                 base(c) * 16, 0);
+                                                 base(c) * 16, kNT);
     }
     for (int k = tid; k < a.K; k += kLrowRegThreads) a.s_out[t * a.K + k] = 0.f;
     if (tid == 0) a.lse2[t] = 0.f;
@@ -226,7 +229,7 @@ __global__ void __launch_bounds__(kLrowRegThreads) k_lrow_reg(LrowArgs a) {
   u32x4 v[PER];
 #pragma unroll
   for (int c = 0; c < PER; ++c)
-    v[c] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rz, voff, base(c) * 16, 0));
+    v[c] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rz, voff, base(c) * 16, kNT));
   float m = -INFINITY, l = 0.f;
 #pragma unroll
   for (int c = 0; c < PER; ++c) {
@@ -272,7 +275,7 @@ __global__ void __launch_bounds__(kLrowRegThreads) k_lrow_reg(LrowArgs a) {
     IO::unpack(v[c], x);
 #pragma unroll
     for (int j = 0; j < 8; ++j) x[j] = coef * fast_exp2(fmaf(x[j], a.c, -lse2));
-    if (in_row(c)) __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, IO::pack(x)), rd, voff, base(c) * 16, 0);
+    if (in_row(c)) __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, IO::pack(x)), rd, voff, base(c) * 16, kNT);
   }
   __syncthreads();  // the dense values of this row are written before the patches
   for (int k = tid; k < a.K; k += kLrowRegThreads) {

@@ -84,9 +84,9 @@ __device__ __forceinline__ int block_count(int v, int* red) {
   return s;
 }
 
-// the 8 keys of vector i of the row
+// the 8 keys of vector i of the row (a streaming read: nontemporal)
 __device__ __forceinline__ void load_keys(const uint16_t* row, int64_t i, uint32_t (&k)[8]) {
-  const u32x4 v = reinterpret_cast<const u32x4*>(row)[i];
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row) + i);
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     k[2 * q] = bf16_key(v[q] & 0xFFFFu);
@@ -142,7 +142,7 @@ __global__ void __launch_bounds__(kTopkThreads) k_topk(TopkArgs a) {
     for (int u = 0; u < kAhead; ++u) {
       const int64_t i = i0 + (int64_t)u * kTopkThreads;
       // past the row: the floor pattern, which changes no kept key
-      v[u] = i < nvec ? reinterpret_cast<const u32x4*>(row)[i] : u32x4{~0u, ~0u, ~0u, ~0u};
+      v[u] = i < nvec ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row) + i) : u32x4{~0u, ~0u, ~0u, ~0u};
     }
 #pragma unroll
     for (int u = 0; u < kAhead; ++u)
