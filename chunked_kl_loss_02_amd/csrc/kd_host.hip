@@ -268,6 +268,30 @@ void launch_prep(Launcher& L, const Plan& P, const Inputs& in, const Bufs& b, bo
   });
 }
 
+// s[t,k] = <h_t, W_idx[t,k]>: the register-row variant for H <= 8192.
+void launch_gather(Launcher& L, const Inputs& in, int64_t T, int64_t H, int64_t V, int K, float* s_out) {
+  using namespace kd;
+  hipStream_t s = L.s;
+  const unsigned g = (unsigned)T;
+  const int64_t nj = cdiv(H, 512);
+  L.run(1, [&] {
+    if (nj <= 2)
+      k_gather_r<2><<<g, 256, 0, s>>>(in.h, in.W, in.idx, in.mask, T, H, V, K, s_out);
+    else if (nj <= 4)
+      k_gather_r<4><<<g, 256, 0, s>>>(in.h, in.W, in.idx, in.mask, T, H, V, K, s_out);
+    else if (nj <= 6)
+      k_gather_r<6><<<g, 256, 0, s>>>(in.h, in.W, in.idx, in.mask, T, H, V, K, s_out);
+    else if (nj <= 8)
+      k_gather_r<8><<<g, 256, 0, s>>>(in.h, in.W, in.idx, in.mask, T, H, V, K, s_out);
+    else if (nj <= 12)
+      k_gather_r<12><<<g, 256, 0, s>>>(in.h, in.W, in.idx, in.mask, T, H, V, K, s_out);
+    else if (nj <= 16)
+      k_gather_r<16><<<g, 256, 0, s>>>(in.h, in.W, in.idx, in.mask, T, H, V, K, s_out);
+    else
+      k_gather<<<g, 256, 0, s>>>(in.h, in.W, in.idx, in.mask, T, H, V, K, s_out);
+  });
+}
+
 // Gather, pass 1 (per-token log-sum-exp), per-row loss and the mean.
 void launch_forward(Launcher& L, const Plan& P, const Inputs& in, const Bufs& b, float* loss, float* row_loss) {
   hipStream_t s = L.s;
@@ -275,7 +299,7 @@ void launch_forward(Launcher& L, const Plan& P, const Inputs& in, const Bufs& b,
   const int64_t T = P.T, H = P.H, V = P.V;
   const int K = P.K;
   const float c = kLog2e / P.tau;
-  L.run(1, [&] { k_gather<<<(unsigned)T, 256, 0, s>>>(in.h, in.W, in.idx, in.mask, T, H, V, K, b.s); });
+  launch_gather(L, in, T, H, V, K, b.s);
   for (int64_t t0 = 0; t0 < T; t0 += P.Tb) {
     const int64_t rows = std::min<int64_t>(P.Tb, T - t0);
     Pass1Args a{};

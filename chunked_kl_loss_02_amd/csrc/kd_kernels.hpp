@@ -179,6 +179,57 @@ __global__ void __launch_bounds__(256) k_gather(const uint16_t* __restrict__ h, 
   }
 }
 
+// The same with the token's h row held in registers (H <= 512 * NJ) and two
+// cached entries per wave at a time, their W rows read with nontemporal
+// loads (a row is read once per entry that names it).
+template <int NJ>
+__global__ void __launch_bounds__(256) k_gather_r(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W,
+                                                  const int32_t* __restrict__ idx, const uint8_t* __restrict__ mask,
+                                                  int64_t T, int64_t H, int64_t V, int K, float* __restrict__ s_out) {
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t t = blockIdx.x;
+  if (t >= T) return;
+  const bool keep = mask ? mask[t] != 0 : true;
+  const __amdgpu_buffer_rsrc_t rh = make_rsrc(h + t * H, (uint64_t)H * 2);
+  u32x4 hv[NJ];  // vector lane + 64 jj of the row; zeros past H
+#pragma unroll
+  for (int jj = 0; jj < NJ; ++jj) hv[jj] = buf_load16(rh, (uint32_t)(lane + 64 * jj) * 16u);
+  for (int k = w; k < K; k += 8) {
+    const int k2 = k + 4;
+    const int32_t v0 = __builtin_amdgcn_readfirstlane(idx[t * K + k]);
+    const int32_t v1 = k2 < K ? __builtin_amdgcn_readfirstlane(idx[t * K + k2]) : -1;
+    const bool ok0 = keep && v0 >= 0 && (int64_t)v0 < V;
+    const bool ok1 = keep && v1 >= 0 && (int64_t)v1 < V;
+    // an entry that is dropped reads nothing (empty range) and sums to 0
+    const __amdgpu_buffer_rsrc_t r0 = make_rsrc(ok0 ? W + (int64_t)v0 * H : W, ok0 ? (uint64_t)H * 2 : 0);
+    const __amdgpu_buffer_rsrc_t r1 = make_rsrc(ok1 ? W + (int64_t)v1 * H : W, ok1 ? (uint64_t)H * 2 : 0);
+    u32x4 b0[NJ], b1[NJ];
+#pragma unroll
+    for (int jj = 0; jj < NJ; ++jj) {
+      const int o = (lane + 64 * jj) * 16;
+      b0[jj] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r0, o, 0, 2));
+      b1[jj] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r1, o, 0, 2));
+    }
+    float acc0 = 0.f, acc1 = 0.f;
+#pragma unroll
+    for (int jj = 0; jj < NJ; ++jj)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float hl = bf16_to_f32(hv[jj][q] & 0xFFFFu), hh = bf16_to_f32(hv[jj][q] >> 16);
+        acc0 = fmaf(hl, bf16_to_f32(b0[jj][q] & 0xFFFFu), acc0);
+        acc0 = fmaf(hh, bf16_to_f32(b0[jj][q] >> 16), acc0);
+        acc1 = fmaf(hl, bf16_to_f32(b1[jj][q] & 0xFFFFu), acc1);
+        acc1 = fmaf(hh, bf16_to_f32(b1[jj][q] >> 16), acc1);
+      }
+    acc0 = wave_sum(acc0);
+    acc1 = wave_sum(acc1);
+    if (lane == 0) {
+      s_out[t * K + k] = acc0;
+      if (k2 < K) s_out[t * K + k2] = acc1;
+    }
+  }
+}
+
 // ----------------------------------------------------------------- pass 1
 // Grid: padded to a multiple of 8; work id -> (token tile, vocabulary tile),
 // both of 256.  Each workgroup writes one (max, sum) pair per token of its

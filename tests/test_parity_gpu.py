@@ -111,6 +111,15 @@ def test_realistic_hidden_size():
     check(got, ref)
 
 
+def test_wide_hidden_sizes():
+    # the teacher-id gather holds h rows of up to 8192 in registers (H = 4160
+    # and 8192 there) and loops over longer rows (H = 8256)
+    for T, H, seed in ((40, 4160, 11), (24, 8192, 12), (24, 8256, 13)):
+        x = make(T, H, 700, 8, seed)
+        got, ref = run_case(x, 1.0)
+        check(got, ref)
+
+
 def test_duplicates_and_neg_inf_logits():
     x = make(64, 128, 1000, 8, 5)
     x["teacher_idx"][0, 1] = x["teacher_idx"][0, 0]
