@@ -319,7 +319,7 @@ void launch_forward(Launcher& L, const Plan& P, const Inputs& in, const Bufs& b,
     const int grid = (int)(cdiv(a.total, 8) * 8);
     L.run(2, [&] { k_pass1<false><<<grid, 256, 0, s>>>(a); });
     L.run(3, [&] {
-      k_lse<<<(unsigned)cdiv(rows, 32), 256, 0, s>>>(b.part, P.nranges, (int)P.ldp, rows, b.lse2 + t0);
+      k_lse<<<(unsigned)cdiv(rows, kLseTok), 256, 0, s>>>(b.part, P.nranges, (int)P.ldp, rows, b.lse2 + t0);
     });
   }
   const int64_t nb = cdiv(T, 256);
@@ -477,7 +477,7 @@ void launch_seq(Launcher& L, const Plan& P, uint32_t flags, const Inputs& in, co
     const int grid = (int)(cdiv(a.total, 8) * 8);
     L.run(2, [&] { k_pass1<true><<<grid, 256, 0, s>>>(a); });
     L.run(3, [&] {
-      k_lse<<<(unsigned)cdiv(rows, 32), 256, 0, s>>>(b.part, P.nranges, (int)P.ldp, rows, b.lse2 + t0);
+      k_lse<<<(unsigned)cdiv(rows, kLseTok), 256, 0, s>>>(b.part, P.nranges, (int)P.ldp, rows, b.lse2 + t0);
     });
     L.run(1, [&] {
       k_gather_s<<<(unsigned)cdiv(rows * K, 256), 256, 0, s>>>(St, lds, in.idx + t0 * K,

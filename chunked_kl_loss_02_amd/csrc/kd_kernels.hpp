@@ -384,25 +384,39 @@ __global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 
 }
 
 // lse2[t] = log2 sum_v 2^(c S[t,v]) from the per-tile partials.  A block
-// handles 32 tokens; its 8 thread groups each fold every 8th tile, then the
-// 8 partial results are folded in a fixed order (deterministic).
+// handles 16 tokens; its 16 thread groups each fold every 16th tile (four
+// loads in flight), then the 16 partial results are folded in a fixed order
+// (deterministic).
+constexpr int kLseTok = 16, kLseGroups = 16;
 __global__ void __launch_bounds__(256) k_lse(const float2* __restrict__ part, int nranges, int ldp, int64_t rows,
                                              float* __restrict__ lse2) {
-  __shared__ float2 red[8][32];
-  const int tx = threadIdx.x & 31, g = threadIdx.x >> 5;
-  const int64_t t = (int64_t)blockIdx.x * 32 + tx;
+  __shared__ float2 red[kLseGroups][kLseTok];
+  const int tx = threadIdx.x % kLseTok, g = threadIdx.x / kLseTok;
+  const int64_t t = (int64_t)blockIdx.x * kLseTok + tx;
   float m = -INFINITY, l = 0.f;
   if (t < rows) {
-    for (int r = g; r < nranges; r += 8) {
-      const float2 p = part[(int64_t)r * ldp + t];
-      lse_merge(m, l, p.x, p.y);
+    float m2 = -INFINITY, l2 = 0.f;
+    int r = g;
+    for (; r + 3 * kLseGroups < nranges; r += 4 * kLseGroups) {
+      float2 q[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) q[u] = part[(int64_t)(r + u * kLseGroups) * ldp + t];
+      lse_merge(m, l, q[0].x, q[0].y);
+      lse_merge(m2, l2, q[1].x, q[1].y);
+      lse_merge(m, l, q[2].x, q[2].y);
+      lse_merge(m2, l2, q[3].x, q[3].y);
     }
+    for (; r < nranges; r += kLseGroups) {
+      const float2 q = part[(int64_t)r * ldp + t];
+      lse_merge(m, l, q.x, q.y);
+    }
+    lse_merge(m, l, m2, l2);
   }
   red[g][tx] = make_float2(m, l);
   __syncthreads();
   if (g == 0 && t < rows) {
 #pragma unroll
-    for (int k = 1; k < 8; ++k) lse_merge(m, l, red[k][tx].x, red[k][tx].y);
+    for (int k = 1; k < kLseGroups; ++k) lse_merge(m, l, red[k][tx].x, red[k][tx].y);
     lse2[t] = m + log2f(l);
   }
 }
