@@ -12,7 +12,7 @@
 //                      tile's (max, sum 2^(c S - max))
 //            k_lse     merges the per-tile partials -> lse2[t] (log2 units)
 //   teacher: k_teacher p = softmax_K(u/tau), merged mass of duplicate ids,
-//                      sum_k p log(mass) per row; k_gather s[t,k] = S[t, idx]
+//                      sum_k p log(mass) per row; k_gather(_r) s[t,k] = S[t, idx]
 //   loss   : k_rows / k_sum   KL_t = sum p log p - sum p s / tau + LSE_t
 //   pass 2 : k_pass2   recomputes the S^T tile, writes the logit gradient
 //                      G = coef * 2^(c S - lse2) (bf16) for one (token block,
