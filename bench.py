@@ -299,8 +299,8 @@ def main():
     ap.add_argument("--sweep", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(the loss shards along tokens; see the design notes). Use --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              "(the loss would shard along tokens). Use --gpus 1.", file=sys.stderr)
         sys.exit(2)
     if args.copy_probe:
         copy_probe()

@@ -1,4 +1,4 @@
-"""Numbers the pages print, checked against the formulas this build reports."""
+"""Numbers the pages print, checked against the oracle's formulas and the bench's reporting."""
 import json
 import os
 
