@@ -173,8 +173,8 @@ __device__ __forceinline__ void mfma_substep(f32x16 (&acc)[MI][NI], const bf16x8
 }
 
 // Instruction-order hints for one scheduling region: per sub-step, its MFMAs
-// with, one after each MFMA, the next sub-step's fragment reads and then this
-// k-step's global loads.
+// with, one after each MFMA, the next sub-step's fragment reads and then the
+// global loads issued in the region.
 template <int NM, int NR, int NV>
 __device__ __forceinline__ void sched_substep() {
   if constexpr (NM > 0) {
@@ -186,7 +186,6 @@ __device__ __forceinline__ void sched_substep() {
   }
 }
 
-__device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 __device__ __forceinline__ void wait_all() { asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory"); }
 
 // One k-step over stage (ca, cb), whose successor (na, nb) is already in
