@@ -120,6 +120,13 @@ def test_wide_hidden_sizes():
         check(got, ref)
 
 
+def test_largest_supported_k():
+    # K = 1024, the most cached entries per token the teacher kernel takes
+    x = make(40, 128, 3000, 1024, 14, mask="packed8")
+    got, ref = run_case(x, 1.0, chunk_v=1024)
+    check(got, ref)
+
+
 def test_duplicates_and_neg_inf_logits():
     x = make(64, 128, 1000, 8, 5)
     x["teacher_idx"][0, 1] = x["teacher_idx"][0, 0]

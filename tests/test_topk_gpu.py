@@ -28,7 +28,7 @@ def check(Xf, K):
     assert np.array_equal(gv.astype(np.float64), ref_val)
 
 
-@pytest.mark.parametrize("V,K", [(4096, 64), (8800, 100), (8, 8), (2048, 1), (512, 512)])
+@pytest.mark.parametrize("V,K", [(4096, 64), (8800, 100), (8, 8), (2048, 1), (512, 512), (5000, 1024)])
 def test_random_rows(V, K):
     r = np.random.default_rng(V + K)
     check(synth.round_bf16_np((r.standard_normal((67, V)) * 2).astype(np.float32)), K)
