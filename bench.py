@@ -32,9 +32,9 @@ METRIC = "tokens/s fwd+bwd fused chunked KL (H=2880,V=201088,K=64); MFMA util; p
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "bwd_traffic_gptoss.json")
+# the sources k_bwd is built and launched from (the traffic summary is its)
 KERNEL_SOURCES = [os.path.join(ROOT, "chunked_kl_loss_02_amd", "csrc", f)
-                  for f in ("kd_common.hpp", "kd_gemm.hpp", "kd_kernels.hpp", "kd_logits.hpp", "kd_topk.hpp",
-                            "kd_host.hip")]
+                  for f in ("kd_common.hpp", "kd_gemm.hpp", "kd_kernels.hpp", "kd_host.hip")]
 
 
 def naive_logit_bytes(T: int, V: int, itemsize: int = 2) -> int:

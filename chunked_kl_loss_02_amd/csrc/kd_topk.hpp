@@ -136,14 +136,7 @@ __global__ void __launch_bounds__(kTopkThreads) k_topk(TopkArgs a) {
   int p_lo = 0, p_hi = 0;
   constexpr int kAhead = 4;  // vectors in flight per thread
   int pos = 0;
-  for (int64_t i0 = tid; i0 < nvec; i0 += (int64_t)kAhead * kTopkThreads) {
-    u32x4 v[kAhead];
-#pragma unroll
-    for (int u = 0; u < kAhead; ++u) {
-      const int64_t i = i0 + (int64_t)u * kTopkThreads;
-      // past the row: the floor pattern, which changes no kept key
-      v[u] = i < nvec ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row) + i) : u32x4{~0u, ~0u, ~0u, ~0u};
-    }
+  auto fold = [&](const u32x4 (&v)[kAhead]) {
 #pragma unroll
     for (int u = 0; u < kAhead; ++u)
 #pragma unroll
@@ -157,6 +150,25 @@ __global__ void __launch_bounds__(kTopkThreads) k_topk(TopkArgs a) {
         m1 = n1;
         m2 = pk_max_u16(lo, m2);
       }
+  };
+  const u32x4* rv = reinterpret_cast<const u32x4*>(row);
+  int64_t i0 = tid;
+  // whole groups of kAhead vectors: no bounds tests
+  for (; i0 + (int64_t)(kAhead - 1) * kTopkThreads < nvec; i0 += (int64_t)kAhead * kTopkThreads) {
+    u32x4 v[kAhead];
+#pragma unroll
+    for (int u = 0; u < kAhead; ++u) v[u] = __builtin_nontemporal_load(rv + i0 + (int64_t)u * kTopkThreads);
+    fold(v);
+  }
+  // the last, partial group: past the row the floor pattern, which changes no kept key
+  if (i0 < nvec) {
+    u32x4 v[kAhead];
+#pragma unroll
+    for (int u = 0; u < kAhead; ++u) {
+      const int64_t i = i0 + (int64_t)u * kTopkThreads;
+      v[u] = i < nvec ? __builtin_nontemporal_load(rv + i) : u32x4{~0u, ~0u, ~0u, ~0u};
+    }
+    fold(v);
   }
   if (tid == 0) {
     ncand = 0;
