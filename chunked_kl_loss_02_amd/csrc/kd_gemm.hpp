@@ -4,11 +4,13 @@
 // owns a (32*MI) x (32*NI) block of the output tile, held in MI*NI
 // v_mfma_f32_32x32x16_bf16 accumulators (16 fp32 per lane each).  K advances
 // 64 at a time (four MFMA sub-steps of 16) through two LDS stages per
-// operand, with one barrier per step between sub-steps 2 and 3: sub-step 3's
-// fragments are already in registers by then, so its MFMAs cover the fetch
-// of the next stage's first fragments after the barrier.  The barrier also
-// frees the stage just consumed, and the loads of the step after next go
-// into it right away, so global data has a full step of MFMAs to arrive.
+// operand, with one barrier per step, in the middle: each sub-step has its
+// own set of fragment registers, sub-steps 2 and 3 read theirs under the
+// MFMAs of sub-steps 0 and 1, and after the barrier the MFMAs of sub-steps 2
+// and 3 cover the fetch of the next stage's first two sub-steps.  The
+// barrier also frees the stage just consumed, and the loads of the step
+// after next go into it right away, so global data has a full step of MFMAs
+// to arrive.
 //
 // Operands are loaded with raw buffer loads whose range ends exactly at the
 // last valid row: out-of-range rows read as zero, which covers the ragged
@@ -172,9 +174,9 @@ __device__ __forceinline__ void mfma_substep(f32x16 (&acc)[MI][NI], const bf16x8
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
 }
 
-// Instruction-order hints for one scheduling region: per sub-step, its MFMAs
-// with, one after each MFMA, the next sub-step's fragment reads and then the
-// global loads issued in the region.
+// Instruction-order hints for one scheduling region of NM MFMAs: one after
+// each MFMA, the region's fragment reads (NR, in order) and then its global
+// loads (NV), one per MFMA.
 template <int NM, int NR, int NV>
 __device__ __forceinline__ void sched_substep() {
   if constexpr (NM > 0) {
@@ -189,37 +191,34 @@ __device__ __forceinline__ void sched_substep() {
 __device__ __forceinline__ void wait_all() { asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory"); }
 
 // One k-step over stage (ca, cb), whose successor (na, nb) is already in
-// flight:
-//   region 1: sub-steps 0..2, their MFMAs interleaved with the fragment reads
-//             of sub-steps 1..3; then wait for this wave's loads into (na, nb)
-//             and its LDS reads, and meet the other waves;
+// flight; fragment set s (a[s], b[s]) holds sub-step s:
+//   region 1: the MFMAs of sub-steps 0 and 1 interleaved with the fragment
+//             reads of sub-steps 2 and 3; then wait for this wave's loads
+//             into (na, nb) and its LDS reads, and meet the other waves;
 //   region 2: (ca, cb) is free: the loads of step kn go into it, and the
-//             first fragments of (na, nb) load, under sub-step 3's MFMAs
-//             (their fragments are already in registers).
-// On entry a[0], b[0] hold sub-step 0 of (ca, cb); on exit of (na, nb).
+//             fragments of sub-steps 0 and 1 of (na, nb) load, under the
+//             MFMAs of sub-steps 2 and 3.
+// On entry sets 0 and 1 hold sub-steps 0 and 1 of (ca, cb); on exit of (na, nb).
 template <int MI, int NI, class LA, class LB>
 __device__ __forceinline__ void kstep(LA& la, LB& lb, int kn, uint16_t* ca, uint16_t* cb, const uint16_t* na,
-                                      const uint16_t* nb, f32x16 (&acc)[MI][NI], bf16x8 (&a)[2][MI],
-                                      bf16x8 (&b)[2][NI], int arow0, int brow0, int lane) {
+                                      const uint16_t* nb, f32x16 (&acc)[MI][NI], bf16x8 (&a)[4][MI],
+                                      bf16x8 (&b)[4][NI], int arow0, int brow0, int lane) {
   constexpr int NM = MI * NI, NR = MI * LA::kReads + NI * LB::kReads;
   constexpr int NVM = LA::kVmem + LB::kVmem;
-  static_assert(NR <= NM, "more fragment reads than MFMAs in a sub-step");
-  static_assert(NVM <= NM, "more loads than MFMAs in a sub-step");
-#pragma unroll
-  for (int s = 0; s < 3; ++s) {
-    load_frags<MI, NI, LA, LB>(ca, cb, a[(s + 1) & 1], b[(s + 1) & 1], arow0, brow0, lane, s + 1);
-    mfma_substep<MI, NI>(acc, a[s & 1], b[s & 1]);
-  }
-  sched_substep<NM, NR, 0>();
-  sched_substep<NM, NR, 0>();
-  sched_substep<NM, NR, 0>();
+  load_frags<MI, NI, LA, LB>(ca, cb, a[2], b[2], arow0, brow0, lane, 2);
+  load_frags<MI, NI, LA, LB>(ca, cb, a[3], b[3], arow0, brow0, lane, 3);
+  mfma_substep<MI, NI>(acc, a[0], b[0]);
+  mfma_substep<MI, NI>(acc, a[1], b[1]);
+  sched_substep<2 * NM, 2 * NR, 0>();
   wait_all();
   __syncthreads();
   la.issue(kn, ca);
   lb.issue(kn, cb);
   load_frags<MI, NI, LA, LB>(na, nb, a[0], b[0], arow0, brow0, lane, 0);
-  mfma_substep<MI, NI>(acc, a[1], b[1]);
-  sched_substep<NM, NR, NVM>();
+  load_frags<MI, NI, LA, LB>(na, nb, a[1], b[1], arow0, brow0, lane, 1);
+  mfma_substep<MI, NI>(acc, a[2], b[2]);
+  mfma_substep<MI, NI>(acc, a[3], b[3]);
+  sched_substep<2 * NM, 2 * NR, NVM>();
 }
 
 // Full K loop for one output tile: acc = A_tile * B_tile^T over nk steps,
@@ -240,7 +239,7 @@ __device__ __forceinline__ void gemm_tile(LA& la, LB& lb, int nk, const Stages& 
 #pragma unroll
     for (int j = 0; j < NI; ++j) acc[i][j] = f32x16{};
   if (nk <= 0) return;
-  bf16x8 a[2][MI], b[2][NI];
+  bf16x8 a[4][MI], b[4][NI];
   // an odd step count starts in the second half of the loop body (step 0 in
   // stage 1), so that one loop body, with no separate tail, runs every step
   const bool odd = nk & 1;
@@ -254,6 +253,7 @@ __device__ __forceinline__ void gemm_tile(LA& la, LB& lb, int nk, const Stages& 
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(NVM) : "memory");
   __syncthreads();
   load_frags<MI, NI, LA, LB>(sa, sb, a[0], b[0], arow0, brow0, lane, 0);
+  load_frags<MI, NI, LA, LB>(sa, sb, a[1], b[1], arow0, brow0, lane, 1);
   const int last = nk - 1;
   for (int kt = odd ? -1 : 0; kt < last; kt += 2) {
     if (kt >= 0) kstep<MI, NI>(la, lb, kt + 2 < nk ? kt + 2 : last, st.a0, st.b0, st.a1, st.b1, acc, a, b, arow0, brow0, lane);
