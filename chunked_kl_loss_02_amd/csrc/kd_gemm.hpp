@@ -174,32 +174,22 @@ __device__ __forceinline__ void mfma_substep(f32x16 (&acc)[MI][NI], const bf16x8
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
 }
 
-// Instruction-order hints for one scheduling region of NM MFMAs: one after
-// each MFMA, the region's fragment reads (NR, in order) and then its global
-// loads (NV), one per MFMA.
-template <int NM, int NR, int NV>
-__device__ __forceinline__ void sched_substep() {
+// Instruction-order hints spread evenly over a region of NM MFMAs: after
+// every second MFMA one of the region's NR fragment reads (after every MFMA
+// once more reads remain than every second one can take) and after the
+// others one of its NV global loads.  Bunched instead (the reads one per
+// MFMA from the start, the loads one per MFMA in the first half) pass 1 ran
+// 4 %, pass 2 5 % and k_bwd 1-5 % slower: issuing many memory instructions
+// back to back holds up the MFMAs behind them.
+template <int NM, int NR, int NV, int Q = 0>
+__device__ __forceinline__ void sched_even() {
   if constexpr (NM > 0) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    if constexpr (NR > 0) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    if constexpr (NV > 0 && (NR <= 0 || NR < NM)) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
-    constexpr int nv = (NV > 0 && (NR <= 0 || NR < NM)) ? NV - 1 : NV;
-    sched_substep<NM - 1, (NR > 0 ? NR - 1 : 0), nv>();
-  }
-}
-
-// The same for region 2, with the global loads spread out: after every MFMA
-// a fragment read while any remain, and after every second MFMA a global
-// load while any remain (16 loads over 32 MFMAs; bunching them into the
-// first half, one per MFMA, ran k_bwd 4.6 % and the step 3.8 % slower).
-template <int NM, int NR, int NV, int Q>
-__device__ __forceinline__ void sched_spread() {
-  if constexpr (NM > 0) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    if constexpr (NR > 0) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    constexpr bool r = NR > 0 && ((Q & 1) == 0 || 2 * NR > NM);
+    if constexpr (r) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     constexpr bool v = NV > 0 && (Q & 1);
     if constexpr (v) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
-    sched_spread<NM - 1, (NR > 0 ? NR - 1 : 0), (v ? NV - 1 : NV), Q + 1>();
+    sched_even<NM - 1, (r ? NR - 1 : NR), (v ? NV - 1 : NV), Q + 1>();
   }
 }
 
@@ -224,7 +214,7 @@ __device__ __forceinline__ void kstep(LA& la, LB& lb, int kn, uint16_t* ca, uint
   load_frags<MI, NI, LA, LB>(ca, cb, a[3], b[3], arow0, brow0, lane, 3);
   mfma_substep<MI, NI>(acc, a[0], b[0]);
   mfma_substep<MI, NI>(acc, a[1], b[1]);
-  sched_substep<2 * NM, 2 * NR, 0>();
+  sched_even<2 * NM, 2 * NR, 0>();
   wait_all();
   __syncthreads();
   la.issue(kn, ca);
@@ -233,7 +223,7 @@ __device__ __forceinline__ void kstep(LA& la, LB& lb, int kn, uint16_t* ca, uint
   load_frags<MI, NI, LA, LB>(na, nb, a[1], b[1], arow0, brow0, lane, 1);
   mfma_substep<MI, NI>(acc, a[2], b[2]);
   mfma_substep<MI, NI>(acc, a[3], b[3]);
-  sched_spread<2 * NM, 2 * NR, NVM, 0>();
+  sched_even<2 * NM, 2 * NR, NVM>();
 }
 
 // Full K loop for one output tile: acc = A_tile * B_tile^T over nk steps,
