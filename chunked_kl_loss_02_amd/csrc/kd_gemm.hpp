@@ -174,22 +174,24 @@ __device__ __forceinline__ void mfma_substep(f32x16 (&acc)[MI][NI], const bf16x8
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
 }
 
-// Instruction-order hints spread evenly over a region of NM MFMAs: after
-// every second MFMA one of the region's NR fragment reads (after every MFMA
-// once more reads remain than every second one can take) and after the
-// others one of its NV global loads.  Bunched instead (the reads one per
-// MFMA from the start, the loads one per MFMA in the first half) pass 1 ran
-// 4 %, pass 2 5 % and k_bwd 1-5 % slower: issuing many memory instructions
-// back to back holds up the MFMAs behind them.
-template <int NM, int NR, int NV, int Q = 0>
+// Instruction-order hints spread evenly over a region of NM MFMAs: its NR
+// fragment reads and NV global loads follow the MFMAs at evenly spaced
+// positions (16 reads and 16 loads over 32 MFMAs alternate; 24 reads take 3
+// of every 4).  Bunched instead (the reads one per MFMA from the start, the
+// loads one per MFMA in the first half) pass 1 ran 4 %, pass 2 5 % and k_bwd
+// 1-5 % slower: many memory instructions issued back to back hold up the
+// MFMAs behind them.
+template <int NM, int NR, int NV, int Q = 0, int TM = NM, int TR = NR, int TV = NV>
 __device__ __forceinline__ void sched_even() {
   if constexpr (NM > 0) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    constexpr bool r = NR > 0 && ((Q & 1) == 0 || 2 * NR > NM);
-    if constexpr (r) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    constexpr bool v = NV > 0 && (Q & 1);
-    if constexpr (v) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
-    sched_even<NM - 1, (r ? NR - 1 : NR), (v ? NV - 1 : NV), Q + 1>();
+    // Bresenham: the q-th MFMA is followed by the reads and loads whose even
+    // share of the region ends there (loads offset by half a slot)
+    constexpr int r = (Q + 1) * TR / TM - Q * TR / TM;
+    constexpr int v = ((2 * Q + 2) * TV + TM) / (2 * TM) - ((2 * Q) * TV + TM) / (2 * TM);
+    if constexpr (r > 0) __builtin_amdgcn_sched_group_barrier(0x100, r, 0);
+    if constexpr (v > 0) __builtin_amdgcn_sched_group_barrier(0x010, v, 0);
+    sched_even<NM - 1, NR - r, NV - v, Q + 1, TM, TR, TV>();
   }
 }
 
