@@ -120,6 +120,15 @@ def test_wide_hidden_sizes():
         check(got, ref)
 
 
+def test_one_k_step_contractions():
+    # H = 64: the pass GEMMs run a single k-step (their K loop is H / 64), and
+    # with 64 vocabulary rows in the last chunk and 64 tokens so do the
+    # gradient contractions' last launches
+    x = make(64, 64, 1088, 8, 15)
+    got, ref = run_case(x, 1.0, chunk_v=1024)
+    check(got, ref)
+
+
 def test_largest_supported_k():
     # K = 1024, the most cached entries per token the teacher kernel takes
     x = make(40, 128, 3000, 1024, 14, mask="packed8")
