@@ -13,6 +13,13 @@ Other modes (not the benchmark line):
   --copy-probe      a plain device copy of known size, to calibrate rocprofv3
                     FETCH_SIZE / WRITE_SIZE against the algorithmic bytes
   --sweep           tokens/s and peak memory over T in {4096 ... 262144}
+                    (the default run already carries them in "scaling")
+
+The default run also adds "scaling": the long-context head (T 32768, tau 2,
+packed mask), the Qwen-like head and the output-head sweep T in {16384,
+65536, 131072, 262144}, each with tokens/s, TFLOP/s over 8 T H V, peak device
+memory and the naive 2 T V logit bytes; and, in "cpu_baseline", the tiny
+config timed in full through the oracle at one thread and at every core.
 """
 from __future__ import annotations
 
@@ -278,6 +285,96 @@ def run_one(args, wl):
     return res, x
 
 
+def run_scaling_point(args, wl, steps, warmup):
+    """One fused call per step at a larger workload (same kernels and default
+    tiling as the main line): tokens/s, TFLOP/s over 8 T H V, peak device
+    memory of the call (inputs, outputs, workspace) against the 2 T V bytes
+    of one bf16 logit tensor, and the gradient contractions' rate."""
+    import torch
+    import chunked_kl_loss_02_amd as kd
+    import synth
+    dev = torch.device("cuda:0")
+    T, H, V, K, tau = wl.T, wl.H, wl.V, wl.K, wl.tau
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    x = synth.make_inputs_torch(T, H, V, K, seed=args.seed, device=dev, mask=wl.mask)
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    base = torch.cuda.memory_allocated(dev)
+    torch.cuda.reset_peak_memory_stats(dev)
+    ws_bytes = kd.workspace_size(T, H, V, K, tau)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    outs = (torch.empty((), dtype=torch.float32, device=dev),
+            torch.empty((T, H), dtype=torch.float32, device=dev),
+            torch.empty((V, H), dtype=torch.float32, device=dev))
+
+    def step():
+        return kd.fwd_bwd(x["h"], x["W"], x["teacher_idx"], x["teacher_logit"], x["mask"], tau,
+                          workspace=ws, out=outs)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    dt, pk = timed_steps(step, steps, ["bwd"])
+    peak = torch.cuda.max_memory_allocated(dev)
+    inputs = sum(t.numel() * t.element_size() for t in x.values())
+    bwd_ms, bwd_n = pk["bwd"]
+    flops = flops_per_token(H, V) * T
+    res = {"workload": wl.name, "T": T, "H": H, "V": V, "K": K, "tau": tau, "mask": wl.mask,
+           "kept_tokens": int(x["mask"].sum().item()), "steps": steps, "warmup": warmup,
+           "value": T * steps / dt, "unit": "tokens/s", "ms_per_step": dt * 1e3 / steps,
+           "tflops": flops * steps / dt / 1e12, "mfma_frac": flops * steps / dt / 1e12 / PEAK_BF16_TFLOPS,
+           "bwd_tflops": 4.0 * T * H * V * steps / (bwd_ms * 1e-3) / 1e12 if bwd_ms > 0 else 0.0,
+           "peak_mem_bytes": int(peak - base + inputs), "workspace_bytes": int(ws_bytes),
+           "naive_logits_bytes": naive_logit_bytes(T, V), "loss": outs[0].item()}
+    del x, ws, outs
+    torch.cuda.empty_cache()
+    return res
+
+
+def scaling_lines(args):
+    """The output-head scaling sweep (single sequences, H2880 V201088 K64)
+    and the long-context and Qwen-like heads, each timed by the same clock
+    as the main line; fewer steps at the largest T."""
+    import synth
+    out = []
+    pts = [synth.WORKLOADS["long"], synth.WORKLOADS["qwen"]]
+    pts += [synth.Workload(f"sweep-T{T}", T, 2880, 201088, 64, 1.0) for T in synth.SWEEP_T if T != 4096]
+    for wl in pts:
+        steps = 5 if wl.T <= 32768 else 3 if wl.T <= 65536 else 2
+        r = run_scaling_point(args, wl, steps, 1)
+        print(f"[scaling] {wl.name}: {r['value']:.4g} tokens/s, {r['ms_per_step']:.1f} ms/step, "
+              f"peak {r['peak_mem_bytes'] / 1e9:.2f} GB", file=sys.stderr, flush=True)
+        out.append(r)
+    return out
+
+
+def cpu_tiny_full(seconds=3.0):
+    """The tiny config (T128 H256 V4096 K32, tau 1), whole problem, through
+    the fp64 oracle: loss, dH and dW, at one BLAS thread and at every core
+    of this host; repeated for about `seconds` each."""
+    import synth
+    from oracle import kl_dense
+    from threadpoolctl import threadpool_limits, threadpool_info
+    wl = synth.WORKLOADS["tiny"]
+    x = synth.make_inputs_np(wl.T, wl.H, wl.V, wl.K, seed=1, bf16=False)
+    cores = len(os.sched_getaffinity(0))
+    res = {"workload": "tiny T128 H256 V4096 K32 tau1 (fp32 inputs, whole problem, loss + dH + dW)",
+           "unit": "tokens/s", "kind": "oracle"}
+    for key, lim in (("one_thread", 1), ("all_cores", cores)):
+        with threadpool_limits(limits=lim):
+            used = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+            n, t0 = 0, time.perf_counter()
+            while True:
+                kl_dense(x["h"], x["W"], x["teacher_idx"], x["teacher_logit"], x["mask"], wl.tau)
+                n += 1
+                dt = time.perf_counter() - t0
+                if dt >= seconds:
+                    break
+        res[key] = {"value": wl.T * n / dt, "cores": int(used), "calls": n, "seconds": dt}
+    return res
+
+
 def copy_probe(nbytes=1 << 30, reps=5):
     """Plain device-to-device copy of nbytes, for counter calibration."""
     import torch
@@ -302,6 +399,7 @@ def main():
     ap.add_argument("--no-seq-chunk", action="store_true", help="skip the sequence-chunk schedule line")
     ap.add_argument("--no-variants", action="store_true", help="skip the logits / top-K variant lines")
     ap.add_argument("--cpu-rows", type=int, default=2048)
+    ap.add_argument("--no-scaling", action="store_true", help="skip the long / qwen / T-sweep lines")
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--sweep", action="store_true")
     args = ap.parse_args()
@@ -331,8 +429,12 @@ def main():
         res["topk_variant"] = res["logits_variant"].pop("topk_variant")
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(x, wl.tau, args.cpu_rows)
+        res["cpu_baseline"]["tiny_full"] = cpu_tiny_full()
     else:
         res["cpu_baseline"] = None
+    del x
+    if not args.no_scaling and args.workload == "gptoss":
+        res["scaling"] = scaling_lines(args)
     print(json.dumps(res), flush=True)
 
 

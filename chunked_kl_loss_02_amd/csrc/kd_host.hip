@@ -61,6 +61,16 @@ struct Plan {
 constexpr uint32_t kAllFlags =
     KD_FLAG_VALIDATE | KD_FLAG_ACCUMULATE_DH | KD_FLAG_ACCUMULATE_DW | KD_FLAG_GRAD_BF16 | KD_FLAG_SEQ_CHUNK;
 
+// Token block and vocabulary chunk a call uses (the caller's, else the
+// defaults above).  seq: the sequence-chunk schedule (gradient pass only).
+void tiling(const kd_problem* p, bool seq, int64_t* Tb, int64_t* cv) {
+  const int64_t bt = p->block_t ? p->block_t : seq ? kDefaultSeqBlockT : kDefaultBlockT;
+  int64_t tb = p->T < bt ? align256(p->T) : bt;
+  if (tb == 0) tb = 256;
+  *Tb = tb;
+  *cv = p->chunk_v ? p->chunk_v : seq ? kDefaultSeqChunkV : tb <= 4096 ? kDefaultChunkV : kDefaultChunkVLargeBlock;
+}
+
 kd_status check(const kd_problem* p) {
   if (!p) return KD_ERR_ARG;
   if (p->T < 0 || p->H <= 0 || p->V <= 0 || p->K <= 0) return KD_ERR_ARG;
@@ -72,11 +82,15 @@ kd_status check(const kd_problem* p) {
   if (p->K > kd::kTeacherMaxK) return KD_ERR_UNSUPPORTED;
   if (p->chunk_v % 256 != 0 || p->block_t % 256 != 0) return KD_ERR_UNSUPPORTED;
   if (p->V > (int64_t)INT32_MAX || p->T > ((int64_t)1 << 40)) return KD_ERR_UNSUPPORTED;
-  const int64_t cv = p->chunk_v ? p->chunk_v : std::max(kDefaultChunkV, kDefaultSeqChunkV);  // largest default
-  const int64_t bt = p->block_t ? p->block_t : std::max(kDefaultBlockT, kDefaultSeqBlockT);
-  // 32-bit buffer offsets inside one chunk / block operand
+  // Every kernel addresses one chunk or block operand through 32-bit buffer
+  // offsets: the bf16 chunk of W and the token block of h (and its h^T), the
+  // bf16 gradient buffer (block x chunk), and the fp32 gradient targets the
+  // contractions read back and add to (the block's rows of dH, the chunk's
+  // rows of dW, or their fp32 staging for bf16 outputs), 4 bytes an element.
+  int64_t bt, cv;
+  tiling(p, (p->flags & KD_FLAG_SEQ_CHUNK) != 0, &bt, &cv);
   const int64_t lim = (int64_t)UINT32_MAX;
-  if (cv * p->H * 2 > lim || bt * p->H * 2 > lim || bt * cv * 2 > lim) return KD_ERR_UNSUPPORTED;
+  if (cv * p->H * 4 > lim || bt * p->H * 4 > lim || bt * cv * 2 > lim) return KD_ERR_UNSUPPORTED;
   if (256 * p->H * 2 > lim / 2) return KD_ERR_UNSUPPORTED;
   return KD_OK;
 }
@@ -91,13 +105,11 @@ Plan make_plan(const kd_problem* p, bool with_grad = true) {
   P.K = p->K;
   P.tau = p->tau;
   P.seq = with_grad && (p->flags & KD_FLAG_SEQ_CHUNK);
-  P.block_t = p->block_t ? p->block_t : P.seq ? kDefaultSeqBlockT : kDefaultBlockT;
-  P.Tb = P.T < P.block_t ? align256(P.T) : P.block_t;
-  if (P.Tb == 0) P.Tb = 256;
-  P.chunk_v = p->chunk_v              ? p->chunk_v
-              : P.seq                 ? kDefaultSeqChunkV
-              : P.Tb <= 4096          ? kDefaultChunkV
-                                      : kDefaultChunkVLargeBlock;
+  int64_t tb, cv;
+  tiling(p, P.seq, &tb, &cv);
+  P.Tb = tb;
+  P.block_t = (int)(p->block_t ? p->block_t : P.seq ? kDefaultSeqBlockT : kDefaultBlockT);
+  P.chunk_v = (int)cv;
   P.ntt_max = (int)(P.Tb / 256);
   P.nvt = cdiv(P.V, 256);
   P.nranges = (int)P.nvt;

@@ -42,7 +42,11 @@ extern "C" {
 typedef enum kd_status {
   KD_OK = 0,
   KD_ERR_ARG = 1,          /* invalid argument (null pointer, bad size, tau <= 0 ...) */
-  KD_ERR_UNSUPPORTED = 2,  /* valid but not supported: H % 64 != 0, K > 1024, bad alignment */
+  KD_ERR_UNSUPPORTED = 2,  /* valid but not supported: H % 64 != 0, K > 1024, bad alignment,
+                              chunk_v / block_t not multiples of 256, or one chunk or block
+                              too large for 32-bit offsets: chunk_v * H * 4, block_t * H * 4
+                              and block_t * chunk_v * 2 must each be below 4 GiB (the chunk
+                              and block actually used, defaults included) */
   KD_ERR_WORKSPACE = 3,    /* workspace_bytes smaller than kd_topk_kl_workspace_size() */
   KD_ERR_INDEX = 4,        /* (KD_FLAG_VALIDATE) a kept row has a teacher id outside [0, V) */
   KD_ERR_NONFINITE = 5,    /* (KD_FLAG_VALIDATE) a kept row has a NaN/+inf logit or all -inf */

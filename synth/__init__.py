@@ -111,17 +111,18 @@ def _topk_rows_np(S: np.ndarray, K: int):
 
 def make_inputs_np(T: int, H: int, V: int, K: int, seed: int = 0, *,
                    bf16: bool = True, mask: str = "ones",
-                   teacher_noise: float = 1.0) -> dict:
+                   teacher_noise: float = 1.0, logit_scale: float = 2.0) -> dict:
     """Host (numpy) inputs, for shapes the CPU can draw in seconds.
 
-    h ~ N(0,1) [T,H]; W ~ 2*N(0,1)/sqrt(H) [V,H] (student logits std ~2);
+    h ~ N(0,1) [T,H]; W ~ logit_scale*N(0,1)/sqrt(H) [V,H] (student logits
+    std ~ logit_scale: 2 for the workloads, ~10-15 for sharp softmaxes);
     teacher logits = h.W^T (fp32) + teacher_noise*N(0,1); top-K per row.
     With bf16=True h and W are rounded to bf16 first and the teacher is built
     from the rounded values; 'h_bits'/'W_bits' carry the uint16 patterns.
     """
     h = _rng(seed, _S_H).standard_normal((T, H), dtype=np.float32)
     W = (_rng(seed, _S_W).standard_normal((V, H), dtype=np.float32)
-         * np.float32(2.0 / np.sqrt(H)))
+         * np.float32(logit_scale / np.sqrt(H)))
     if bf16:
         h = round_bf16_np(h)
         W = round_bf16_np(W)
@@ -138,7 +139,7 @@ def make_inputs_np(T: int, H: int, V: int, K: int, seed: int = 0, *,
 
 def make_inputs_torch(T: int, H: int, V: int, K: int, seed: int = 0, *,
                       device="cuda", mask: str = "ones", teacher_noise: float = 1.0,
-                      row_chunk: int = 2048) -> dict:
+                      row_chunk: int = 2048, logit_scale: float = 2.0) -> dict:
     """Device inputs for the large workloads (torch is used as a random-number
     and matmul engine here; none of this is the loss).  h, W bf16; teacher
     top-K built in row chunks from bf16 h.W^T (fp32 accumulate) + noise, each
@@ -151,7 +152,7 @@ def make_inputs_torch(T: int, H: int, V: int, K: int, seed: int = 0, *,
     h = torch.randn((T, H), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
     g.manual_seed(1000 * seed + _S_W)
     W = (torch.randn((V, H), generator=g, device=dev, dtype=torch.float32)
-         * (2.0 / np.sqrt(H))).to(torch.bfloat16)
+         * (logit_scale / np.sqrt(H))).to(torch.bfloat16)
     idx = torch.empty((T, K), dtype=torch.int32, device=dev)
     val = torch.empty((T, K), dtype=torch.float32, device=dev)
     for c, t0 in enumerate(range(0, T, row_chunk)):

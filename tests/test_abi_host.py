@@ -84,6 +84,27 @@ def test_chunk_and_block_must_be_multiples_of_256():
     assert _ws(1000, 128, 5000, 8, 1.0, 512, 768)[0] == 0
 
 
+def test_fp32_gradient_targets_must_fit_32_bit_offsets():
+    """The gradient contractions read back and add to fp32 dH / dW rows of
+    one token block / vocabulary chunk through 32-bit byte offsets, so
+    chunk * H * 4 and block * H * 4 must stay below 4 GiB; a problem over
+    that is refused instead of wrapping."""
+    # 12288-row chunk x H = 98304: 2.4 GB of bf16 W rows (under 4 GiB) but
+    # 4.8 GB of fp32 dW rows
+    assert _ws(4096, 98304, 201088, 64)[0] == 2
+    assert _ws(4096, 98304, 201088, 64, 1.0, 12288, 0)[0] == 2
+    assert _ws(4096, 98304, 201088, 64, 1.0, 8192, 0)[0] == 0
+    # one chunk spanning a 262144-token vocabulary at H = 5120 (5.4 GB fp32)
+    assert _ws(512, 5120, 262144, 64, 1.0, 262144, 256)[0] == 2
+    assert _ws(512, 5120, 262144, 64, 1.0, 131072, 256)[0] == 0
+    # a token block of 16384 at H = 65536 (4.3 GB of fp32 dH rows)
+    assert _ws(65536, 65536, 4096, 8, 1.0, 256, 16384)[0] == 2
+    assert _ws(65536, 65536, 4096, 8, 1.0, 256, 8192)[0] == 0
+    # the same bound holds for the split backward and the forward sizes
+    L = kd.lib()
+    assert _size(L.kd_topk_kl_fwd_workspace_size, 512, 5120, 262144, 64, chunk_v=262144, block_t=256)[0] == 2
+
+
 def test_fwd_bwd_rejects_bad_arguments_before_any_hip_call():
     L = kd.lib()
     vp = ctypes.c_void_p

@@ -5,6 +5,7 @@ Protocol (i): full mask; per-row loss, LSE and dH rows of a seeded row sample
 against the oracle on those rows (scaled to the global token count N).
 Protocol (ii): mask restricted to the sample; loss, dH (all rows) and dW (in
 full) against the oracle on the sample.
+Row samples hold 512 tokens (the sample size of the output-head sweep).
 Tolerances as in test_parity_gpu: loss 1e-3 relative, dH/dW 2e-2 normwise."""
 import numpy as np
 import pytest
@@ -38,9 +39,9 @@ def sample_rows(T, n, seed):
     return np.sort(np.random.default_rng(seed).choice(T, size=min(n, T), replace=False))
 
 
-def protocol_i(wl, n_rows=128, seed=7, seq_chunk=False):
-    print(f"[full-i] {wl} seq_chunk={seq_chunk}", flush=True)
-    x = synth.make_inputs_torch(wl.T, wl.H, wl.V, wl.K, seed=3, mask=wl.mask)
+def protocol_i(wl, n_rows=512, seed=7, seq_chunk=False, logit_scale=2.0):
+    print(f"[full-i] {wl} rows={n_rows} seq_chunk={seq_chunk} logit_scale={logit_scale}", flush=True)
+    x = synth.make_inputs_torch(wl.T, wl.H, wl.V, wl.K, seed=3, mask=wl.mask, logit_scale=logit_scale)
     loss, dH, dW, rl, ws = kd.fwd_bwd(x["h"], x["W"], x["teacher_idx"], x["teacher_logit"], x["mask"], wl.tau,
                                       grad_w=False, row_loss=True, return_workspace=True, seq_chunk=seq_chunk)
     lse = kd.lse(ws, wl.T, wl.H, wl.V, wl.K, wl.tau, flags=kd.KD_FLAG_SEQ_CHUNK if seq_chunk else 0)
@@ -68,9 +69,9 @@ def protocol_i(wl, n_rows=128, seed=7, seq_chunk=False):
     assert torch.all(torch.isfinite(dH)).item()
 
 
-def protocol_ii(wl, n_rows=128, seed=11, seq_chunk=False):
-    print(f"[full-ii] {wl} seq_chunk={seq_chunk}", flush=True)
-    x = synth.make_inputs_torch(wl.T, wl.H, wl.V, wl.K, seed=5, mask=wl.mask)
+def protocol_ii(wl, n_rows=512, seed=11, seq_chunk=False, logit_scale=2.0):
+    print(f"[full-ii] {wl} rows={n_rows} seq_chunk={seq_chunk} logit_scale={logit_scale}", flush=True)
+    x = synth.make_inputs_torch(wl.T, wl.H, wl.V, wl.K, seed=5, mask=wl.mask, logit_scale=logit_scale)
     rows = sample_rows(wl.T, n_rows, seed)
     keep = torch.zeros(wl.T, dtype=torch.uint8, device="cuda")
     keep[torch.from_numpy(rows).cuda()] = 1
@@ -127,7 +128,12 @@ def test_qwen_padding_rows():
 
 
 def test_qwen_restricted_mask_full_grads():
-    protocol_ii(synth.WORKLOADS["qwen"], n_rows=96)
+    protocol_ii(synth.WORKLOADS["qwen"])
+
+
+def test_long_context_restricted_mask_full_grads():
+    # dW summed over 4 token blocks of 8192, tau = 2, packed 8-document mask
+    protocol_ii(synth.WORKLOADS["long"])
 
 
 def test_pages_k100_head():
@@ -135,8 +141,27 @@ def test_pages_k100_head():
     protocol_ii(synth.Workload("k100", 1024, 2880, 201088, 100, 1.0), n_rows=64)
 
 
-def test_sweep_largest_T_rows():
-    protocol_i(synth.Workload("sweep-T262144", 262144, 2880, 201088, 64, 1.0), n_rows=128)
+def sweep(T):
+    return synth.Workload(f"sweep-T{T}", T, 2880, 201088, 64, 1.0)
+
+
+@pytest.mark.parametrize("T", [T for T in synth.SWEEP_T if T != 4096])  # 4096 is the gptoss head above
+def test_sweep_rows(T):
+    protocol_i(sweep(T))
+
+
+def test_sweep_largest_T_restricted_mask_full_grads():
+    # dW summed over 32 token blocks, every vocabulary chunk
+    protocol_ii(sweep(262144))
+
+
+@pytest.mark.parametrize("tau", [0.5, 2.0])
+def test_sharp_logits_gptoss_head(tau):
+    # student logits with std ~15: near one-hot softmax over the 201088-word
+    # vocabulary (at tau = 0.5 most exponentials underflow)
+    wl = synth.Workload(f"gptoss-sharp-tau{tau}", 4096, 2880, 201088, 64, tau)
+    protocol_i(wl, logit_scale=15.0)
+    protocol_ii(wl, logit_scale=15.0)
 
 
 def test_peak_memory_linear_in_tokens():
