@@ -11,7 +11,7 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["fwd_bwd", "fwd", "bwd", "topk_kl_loss", "kl_logits", "logits_workspace_size", "KdLogitsProblem",
+__all__ = ["fwd_bwd", "fwd_bwd_noalloc", "NOALLOC_SCRATCH_BYTES", "fwd", "bwd", "topk_kl_loss", "kl_logits", "logits_workspace_size", "KdLogitsProblem",
            "topk_select", "KdTopkProblem", "TopKKLLoss", "workspace_size", "fwd_workspace_size",
            "saved_size", "lse", "saved_lse", "KdProblem", "library_path", "lib", "timing_enable",
            "timing_collect", "KERNEL_CLASSES", "KD_FLAG_VALIDATE", "KD_FLAG_ACCUMULATE_DH",
@@ -27,6 +27,7 @@ KD_FLAG_GRAD_BF16 = 8
 KD_FLAG_SEQ_CHUNK = 16
 ABI_VERSION = 4
 KD_FLAG_LOGITS_F32 = 32
+NOALLOC_SCRATCH_BYTES = 128 << 20  # KD_NOALLOC_SCRATCH_BYTES
 KERNEL_CLASSES = ("teacher", "gather", "pass1", "lse", "loss", "pass2", "fixup", "bwd", "other", "logits", "topk")
 _STATUS = {0: "KD_OK", 1: "KD_ERR_ARG", 2: "KD_ERR_UNSUPPORTED", 3: "KD_ERR_WORKSPACE",
            4: "KD_ERR_INDEX", 5: "KD_ERR_NONFINITE", 6: "KD_ERR_HIP"}
@@ -71,6 +72,8 @@ def lib():
     L.kd_topk_kl_workspace_size.restype = ctypes.c_int
     L.kd_topk_kl_fwd_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.kd_topk_kl_fwd_bwd.restype = ctypes.c_int
+    L.kd_topk_kl_fwd_bwd_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    L.kd_topk_kl_fwd_bwd_noalloc.restype = ctypes.c_int
     for name in ("kd_topk_kl_saved_size", "kd_topk_kl_fwd_workspace_size"):
         getattr(L, name).argtypes = [P, ctypes.POINTER(sz)]
         getattr(L, name).restype = ctypes.c_int
@@ -233,6 +236,31 @@ def fwd_bwd(h, W, teacher_idx, teacher_logit, mask=None, tau=1.0, *, chunk_v=0, 
     if return_workspace:
         res.append(workspace)
     return tuple(res)
+
+
+def fwd_bwd_noalloc(h, W, teacher_idx, teacher_logit, mask=None, tau=1.0, *, out, chunk_v=0, block_t=0,
+                    row_loss=False, validate=False, accumulate_dh=False, accumulate_dw=False, seq_chunk=False):
+    """fwd_bwd through kd_topk_kl_fwd_bwd_noalloc: no workspace and no device
+    allocation (the library's static per-GPU scratch of NOALLOC_SCRATCH_BYTES
+    takes its place).  `out` = preallocated (loss, dH, dW[, row_loss]), dH /
+    dW may be None; they are overwritten (added to with accumulate_*).
+    Returns `out`'s tensors."""
+    import torch
+    T, H, V, K, dev, mask = _check_inputs(h, W, teacher_idx, teacher_logit, mask)
+    loss, dH, dW = out[0], out[1], out[2]
+    rl = out[3] if row_loss else None
+    gdt = dH.dtype if dH is not None else dW.dtype if dW is not None else torch.float32
+    flags = _grad_flags(gdt, accumulate_dh, accumulate_dw) | (KD_FLAG_SEQ_CHUNK if seq_chunk else 0)
+    prob = problem(T, H, V, K, tau, chunk_v, block_t, validate, flags)
+    _check_out(loss, (), torch.float32, dev, "loss")
+    _check_out(dH, (T, H), gdt, dev, "dH")
+    _check_out(dW, (V, H), gdt, dev, "dW")
+    _check_out(rl, (T,), torch.float32, dev, "row_loss")
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    _raise(lib().kd_topk_kl_fwd_bwd_noalloc(ctypes.byref(prob), _ptr(h), _ptr(W), _ptr(teacher_idx),
+                                            _ptr(teacher_logit), _ptr(mask), _ptr(loss), _ptr(dH), _ptr(dW),
+                                            _ptr(rl), ctypes.c_void_p(stream)))
+    return (loss, dH, dW, rl) if row_loss else (loss, dH, dW)
 
 
 def fwd(h, W, teacher_idx, teacher_logit, mask=None, tau=1.0, *, chunk_v=0, block_t=0, row_loss=False,

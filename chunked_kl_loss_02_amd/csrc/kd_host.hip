@@ -5,6 +5,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
 #include <vector>
 
 #include "../../include/kdkl.h"
@@ -593,6 +594,84 @@ kd_status finish(Launcher& L, bool validate, const uint32_t* status) {
   return KD_OK;
 }
 
+// Argument checks of the fused call that need no workspace: synchronous,
+// before anything touches the device.
+kd_status fwd_bwd_args(const kd_problem* p, const uint16_t* h, const uint16_t* W, const int32_t* idx,
+                       const float* logit, const float* loss, const void* dH, const void* dW,
+                       const float* row_loss) {
+  const kd_status st = check(p);
+  if (st != KD_OK) return st;
+  if (!W || !loss) return KD_ERR_ARG;
+  if (p->T > 0 && (!h || !idx || !logit)) return KD_ERR_ARG;
+  if (misaligned(h, 16) || misaligned(W, 16) || misaligned(idx, 4) || misaligned(logit, 4) ||
+      misaligned(dH, 16) || misaligned(dW, 16) || misaligned(loss, 4) || misaligned(row_loss, 4))
+    return KD_ERR_UNSUPPORTED;
+  return KD_OK;
+}
+
+// The fused call's launches over a checked problem and a workspace of at
+// least make_plan(p).total bytes.
+kd_status fwd_bwd_run(const kd_problem* p, const uint16_t* h, const uint16_t* W, const int32_t* teacher_idx,
+                      const float* teacher_logit, const uint8_t* mask, float* loss, void* dH, void* dW,
+                      float* row_loss, void* workspace, hipStream_t stream) {
+  const Plan P = make_plan(p);
+  Launcher L{stream};
+  const Inputs in{h, W, teacher_idx, teacher_logit, mask};
+  const Bufs b = carve(P, workspace, true);
+  const bool validate = (p->flags & KD_FLAG_VALIDATE) != 0;
+  if (P.T == 0) {
+    L.run(8, [&] { kd::k_fill<<<1, 64, 0, L.s>>>(loss, 1, 0.f); });
+    launch_empty_grads(L, P, p->flags, dW);
+    return finish(L, false, nullptr);
+  }
+  launch_prep(L, P, in, b, validate, nullptr);
+  if (P.seq) {
+    float* St = reinterpret_cast<float*>(static_cast<char*>(workspace) + P.o_S);
+    launch_seq(L, P, p->flags, in, b, St, loss, row_loss, dH, dW);
+    return finish(L, validate, b.status);
+  }
+  launch_forward(L, P, in, b, loss, row_loss);
+  if (dH || dW) launch_backward(L, P, p->flags, in, b, dH, dW);
+  return finish(L, validate, b.status);
+}
+
+}  // namespace
+
+// Scratch of kd_topk_kl_fwd_bwd_noalloc, in place of a caller's workspace:
+// one copy per GPU, resident from the library's first use on that GPU until
+// the process ends.  On the host this name is only a stand-in for the
+// symbol; the device address of each GPU's copy comes from
+// hipGetSymbolAddress (scratch_for) and is what the kernels receive.
+static __device__ __align__(256) uint8_t scratch[KD_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices];  // device address of `scratch` on each GPU
+
+// The scratch address on the current device, looked up once per device with
+// that device current.  The stream (NULL = the current device's null
+// stream) must belong to the current device.
+kd_status scratch_for(hipStream_t stream, void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return KD_ERR_HIP;
+  if (dev >= kMaxDevices) return KD_ERR_UNSUPPORTED;
+  if (stream) {
+    hipDevice_t sdev = -1;
+    if (hipStreamGetDevice(stream, &sdev) != hipSuccess) return KD_ERR_HIP;
+    if (sdev != dev) return KD_ERR_ARG;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return KD_ERR_HIP;
+    g_scratch_dev[dev] = ptr;
+  }
+  *out = g_scratch_dev[dev];
+  return KD_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -657,31 +736,26 @@ kd_status kd_topk_kl_fwd_bwd(const kd_problem* p, const uint16_t* h, const uint1
                              const int32_t* teacher_idx, const float* teacher_logit, const uint8_t* mask,
                              float* loss, void* dH, void* dW, float* row_loss, void* workspace,
                              size_t workspace_bytes, void* stream) {
-  kd_status st = check_common(p, h, W, teacher_idx, teacher_logit, workspace);
+  kd_status st = fwd_bwd_args(p, h, W, teacher_idx, teacher_logit, loss, dH, dW, row_loss);
   if (st != KD_OK) return st;
-  if (!loss) return KD_ERR_ARG;
-  if (misaligned(dH, 16) || misaligned(dW, 16) || misaligned(loss, 4) || misaligned(row_loss, 4))
-    return KD_ERR_UNSUPPORTED;
-  const Plan P = make_plan(p);
-  if (workspace_bytes < P.total) return KD_ERR_WORKSPACE;
-  Launcher L{static_cast<hipStream_t>(stream)};
-  const Inputs in{h, W, teacher_idx, teacher_logit, mask};
-  const Bufs b = carve(P, workspace, true);
-  const bool validate = (p->flags & KD_FLAG_VALIDATE) != 0;
-  if (P.T == 0) {
-    L.run(8, [&] { kd::k_fill<<<1, 64, 0, L.s>>>(loss, 1, 0.f); });
-    launch_empty_grads(L, P, p->flags, dW);
-    return finish(L, false, nullptr);
-  }
-  launch_prep(L, P, in, b, validate, nullptr);
-  if (P.seq) {
-    float* St = reinterpret_cast<float*>(static_cast<char*>(workspace) + P.o_S);
-    launch_seq(L, P, p->flags, in, b, St, loss, row_loss, dH, dW);
-    return finish(L, validate, b.status);
-  }
-  launch_forward(L, P, in, b, loss, row_loss);
-  if (dH || dW) launch_backward(L, P, p->flags, in, b, dH, dW);
-  return finish(L, validate, b.status);
+  if (!workspace) return KD_ERR_ARG;
+  if (misaligned(workspace, 256)) return KD_ERR_UNSUPPORTED;
+  if (workspace_bytes < make_plan(p).total) return KD_ERR_WORKSPACE;
+  return fwd_bwd_run(p, h, W, teacher_idx, teacher_logit, mask, loss, dH, dW, row_loss, workspace,
+                     static_cast<hipStream_t>(stream));
+}
+
+kd_status kd_topk_kl_fwd_bwd_noalloc(const kd_problem* p, const uint16_t* h, const uint16_t* W,
+                                     const int32_t* teacher_idx, const float* teacher_logit, const uint8_t* mask,
+                                     float* loss, void* dH, void* dW, float* row_loss, void* stream) {
+  kd_status st = fwd_bwd_args(p, h, W, teacher_idx, teacher_logit, loss, dH, dW, row_loss);
+  if (st != KD_OK) return st;
+  if (make_plan(p).total > (size_t)KD_NOALLOC_SCRATCH_BYTES) return KD_ERR_WORKSPACE;
+  void* ws = nullptr;
+  st = scratch_for(static_cast<hipStream_t>(stream), &ws);
+  if (st != KD_OK) return st;
+  return fwd_bwd_run(p, h, W, teacher_idx, teacher_logit, mask, loss, dH, dW, row_loss, ws,
+                     static_cast<hipStream_t>(stream));
 }
 
 kd_status kd_topk_kl_saved_size(const kd_problem* p, size_t* bytes) {

@@ -125,6 +125,34 @@ kd_status kd_topk_kl_fwd_bwd(const kd_problem* p,
                              float* loss, void* dH, void* dW, float* row_loss,
                              void* workspace, size_t workspace_bytes, void* stream);
 
+/* kd_topk_kl_fwd_bwd without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  It allocates nothing: the library holds
+ * one static device scratch array of KD_NOALLOC_SCRATCH_BYTES per GPU, from
+ * its first use on that GPU until the process ends, and runs the same
+ * kernels with the same tiling as kd_topk_kl_fwd_bwd (bitwise the same
+ * results for the same problem).
+ *
+ *   Arguments as kd_topk_kl_fwd_bwd, minus workspace / workspace_bytes.  The
+ *   stream must belong to the current device (KD_ERR_ARG otherwise).
+ *   A problem whose workspace (kd_topk_kl_workspace_size) exceeds
+ *   KD_NOALLOC_SCRATCH_BYTES returns KD_ERR_WORKSPACE before anything is
+ *   enqueued; the gpt-oss-20b-like head (T 4096, H 2880, V 201088, K 64)
+ *   fits with chunk_v = 8192 (114 MiB).
+ *   The first call on a GPU looks up that GPU's scratch address
+ *   (hipGetSymbolAddress); make it outside graph capture.
+ *   Every call on one GPU uses the same scratch, which keeps the last call's
+ *   contents (nothing in it is assumed zero on entry): calls ordered on one
+ *   stream are safe, calls that may overlap on one GPU (different streams,
+ *   other threads) race on it. */
+#define KD_NOALLOC_SCRATCH_BYTES (128u << 20)
+kd_status kd_topk_kl_fwd_bwd_noalloc(const kd_problem* p,
+                                     const uint16_t* h, const uint16_t* W,
+                                     const int32_t* teacher_idx, const float* teacher_logit,
+                                     const uint8_t* mask,
+                                     float* loss, void* dH, void* dW, float* row_loss,
+                                     void* stream);
+
 /* The same loss split into its two passes, for autograd-style callers (the
  * blog "Making Knowledge Distillation Cheap Enough to Run at Scale", section
  * "Two systems changes": the forward folds each chunk into the running loss

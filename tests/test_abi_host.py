@@ -231,3 +231,21 @@ def test_default_tiling():
     seq = kd.KD_FLAG_SEQ_CHUNK
     assert _size(L.kd_topk_kl_workspace_size, 65536, H, V, K, flags=seq)[1] == \
         _size(L.kd_topk_kl_workspace_size, 65536, H, V, K, flags=seq, chunk_v=16384, block_t=4096)[1]
+
+
+def test_noalloc_rejects_problems_beyond_its_scratch_before_any_hip_call():
+    L = kd.lib()
+    vp = ctypes.c_void_p
+    fake = vp(1 << 20)  # never dereferenced: validation fails first
+    # the gpt-oss head at the default 12288-row chunk needs 146 MiB > 128 MiB
+    p = kd.problem(4096, 2880, 201088, 64)
+    assert _ws(4096, 2880, 201088, 64)[1] > kd.NOALLOC_SCRATCH_BYTES
+    assert L.kd_topk_kl_fwd_bwd_noalloc(ctypes.byref(p), fake, fake, fake, fake, vp(0), fake, fake, fake,
+                                        vp(0), vp(0)) == 3
+    # with 8192-row chunks it fits (checked on the GPU); argument errors come first
+    assert _ws(4096, 2880, 201088, 64, 1.0, 8192, 0)[1] <= kd.NOALLOC_SCRATCH_BYTES
+    assert L.kd_topk_kl_fwd_bwd_noalloc(ctypes.byref(p), fake, vp(0), fake, fake, vp(0), fake, fake, fake,
+                                        vp(0), vp(0)) == 1
+    bad = kd.problem(16, 64, 100, 4, tau=0.0)
+    assert L.kd_topk_kl_fwd_bwd_noalloc(ctypes.byref(bad), fake, fake, fake, fake, vp(0), fake, fake, fake,
+                                        vp(0), vp(0)) == 1
