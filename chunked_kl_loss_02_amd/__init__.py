@@ -65,6 +65,12 @@ def lib():
     if not os.path.exists(library_path):
         raise RuntimeError(f"{library_path} is missing: build it with "
                            "`python -m chunked_kl_loss_02_amd.build` (hipcc, gfx950)")
+    # torch first: its HIP runtime must be the one the library binds to (a
+    # second runtime loaded ahead of torch's sees no device in this process)
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     L = ctypes.CDLL(library_path)
     vp, sz = ctypes.c_void_p, ctypes.c_size_t
     P = ctypes.POINTER(KdProblem)

@@ -56,6 +56,11 @@ struct Plan {
   size_t o_S;        // seq: S^T of one block, [V, Tb] fp32
   size_t o_hT;       // h^T of one token block, [H, Tb] bf16 (gradient pass)
   size_t o_off;      // per-token pass-2 offsets [Tp] (gradient pass)
+  // teacher entries by (token tile, vocabulary tile) (gradient pass):
+  // counts / starts [ntt_all, ldk] then fill cursors [ntt_all, ldk]
+  // (contiguous, cleared together), token-tile bases, entries [T*K]
+  int ntt_all, ldk;
+  size_t o_bcnt, o_bcur, o_bbase, o_ent;
   size_t o_G, o_dhs, o_dws, o_part, o_lse2, o_p, o_pm, o_s, o_neg, o_row, o_bsum, o_scal_f, o_scal_i, o_status, total;
 };
 
@@ -83,6 +88,8 @@ kd_status check(const kd_problem* p) {
   if (p->K > kd::kTeacherMaxK) return KD_ERR_UNSUPPORTED;
   if (p->chunk_v % 256 != 0 || p->block_t % 256 != 0) return KD_ERR_UNSUPPORTED;
   if (p->V > (int64_t)INT32_MAX || p->T > ((int64_t)1 << 40)) return KD_ERR_UNSUPPORTED;
+  // 32-bit positions of the bucketed teacher entries
+  if (p->T * (int64_t)p->K > (int64_t)UINT32_MAX) return KD_ERR_UNSUPPORTED;
   // Every kernel addresses one chunk or block operand through 32-bit buffer
   // offsets: the bf16 chunk of W and the token block of h (and its h^T), the
   // bf16 gradient buffer (block x chunk), and the fp32 gradient targets the
@@ -130,12 +137,20 @@ Plan make_plan(const kd_problem* p, bool with_grad = true) {
   P.o_G = with_grad ? take((size_t)P.grows * P.chunk_v * 2) : 0;
   P.o_hT = with_grad ? take((size_t)P.H * P.Tb * 2) : 0;
   P.o_off = with_grad ? take((size_t)Tp * 4) : 0;
+  P.ntt_all = (int)cdiv(P.T, 256);
+  P.ldk = (int)P.nvt + 1;
+  const size_t nkeys = (size_t)P.ntt_all * P.ldk;
+  P.o_bcnt = with_grad ? take(nkeys * 8) : 0;  // counts then cursors: one region
+  P.o_bcur = P.o_bcnt + nkeys * 4;
+  P.o_bbase = with_grad ? take((size_t)P.ntt_all * 4 + 4) : 0;
+  P.o_ent = with_grad ? take((size_t)P.T * P.K * 4) : 0;
   P.o_S = P.seq ? take((size_t)P.V * P.Tb * 4) : 0;
   const bool stage = with_grad && (p->flags & KD_FLAG_GRAD_BF16);
-  // the sequence-chunk schedule finishes a dW chunk only after the last
-  // block: with several blocks its bf16 staging holds all of dW
-  const bool whole_dw = P.seq && P.T > P.Tb;
-  P.o_dhs = stage ? take((size_t)Tp * P.H * 4) : 0;
+  // both schedules walk token blocks in the outer loop: a block's dH is
+  // final after its last chunk (staged one block at a time), a dW chunk only
+  // after the last block (with several blocks its staging holds all of dW)
+  const bool whole_dw = P.T > P.Tb;
+  P.o_dhs = stage ? take((size_t)(P.seq ? Tp : P.Tb) * P.H * 4) : 0;
   P.o_dws = stage ? take((size_t)(whole_dw ? P.V : P.chunk_v) * P.H * 4) : 0;
   P.o_part = take((size_t)P.nranges * P.ldp * 8);
   P.o_lse2 = take((size_t)Tp * 4);
@@ -213,6 +228,7 @@ struct Bufs {
   uint16_t* G;
   uint16_t* hT;  // h^T of one token block (gradient pass)
   float* off;    // pass-2 offsets (gradient pass)
+  uint32_t *bcnt, *bcur, *bbase, *ent;  // teacher entries by tile (gradient pass)
   float* dhs;   // fp32 staging of a bf16 dH (nullable)
   float* dws;   // fp32 staging of one chunk of a bf16 dW (nullable)
   float2* part;
@@ -234,6 +250,10 @@ Bufs carve(const Plan& P, void* workspace, bool with_grad) {
   b.G = with_grad ? reinterpret_cast<uint16_t*>(ws + P.o_G) : nullptr;
   b.hT = with_grad ? reinterpret_cast<uint16_t*>(ws + P.o_hT) : nullptr;
   b.off = with_grad ? reinterpret_cast<float*>(ws + P.o_off) : nullptr;
+  b.bcnt = with_grad ? reinterpret_cast<uint32_t*>(ws + P.o_bcnt) : nullptr;
+  b.bcur = with_grad ? reinterpret_cast<uint32_t*>(ws + P.o_bcur) : nullptr;
+  b.bbase = with_grad ? reinterpret_cast<uint32_t*>(ws + P.o_bbase) : nullptr;
+  b.ent = with_grad ? reinterpret_cast<uint32_t*>(ws + P.o_ent) : nullptr;
   b.dhs = with_grad && P.o_dhs ? reinterpret_cast<float*>(ws + P.o_dhs) : nullptr;
   b.dws = with_grad && P.o_dws ? reinterpret_cast<float*>(ws + P.o_dws) : nullptr;
   b.part = reinterpret_cast<float2*>(ws + P.o_part);
@@ -351,38 +371,62 @@ void launch_transpose_h(Launcher& L, const Plan& P, const Inputs& in, const Bufs
   L.run(8, [&] { kd::k_transpose_h<<<grid, 256, 0, s>>>(in.h + t0 * P.H, rows, P.H, b.hT, P.Tb); });
 }
 
-// Pass 2: recompute every (block, chunk), form the logit gradient, contract
-// it into dH / dW (fp32 or bf16 per the flags).
+// Teacher entries of kept tokens bucketed by (token tile, vocabulary tile),
+// each with its final logit-gradient value: counts, the two scans, fill.
+void launch_buckets(Launcher& L, const Plan& P, const Inputs& in, const Bufs& b) {
+  hipStream_t s = L.s;
+  using namespace kd;
+  const int64_t T = P.T, n = T * P.K;
+  const int64_t nkeys = (int64_t)P.ntt_all * P.ldk;
+  const float c = kLog2e / P.tau;
+  L.run(6, [&] {
+    k_fill<<<grid_fill(2 * nkeys, 256), 256, 0, s>>>(reinterpret_cast<float*>(b.bcnt), 2 * nkeys, 0.f);
+  });
+  L.run(6, [&] {
+    k_bucket_count<<<(unsigned)cdiv(n, 256), 256, 0, s>>>(in.idx, in.mask, T, P.K, P.V, P.ldk, b.bcnt);
+  });
+  L.run(6, [&] { k_scan_rows<<<(unsigned)P.ntt_all, 1024, 0, s>>>(b.bcnt, (int)P.nvt, P.ldk); });
+  L.run(6, [&] { k_scan_tiles<<<1, 1024, 0, s>>>(b.bcnt, P.ntt_all, P.ldk, (int)P.nvt, b.bbase); });
+  L.run(6, [&] {
+    k_bucket_fill<<<(unsigned)cdiv(n, 256), 256, 0, s>>>(in.idx, b.s, b.pm, b.lse2, in.mask, b.scal_f, T, P.K, P.V,
+                                                         c, P.ldk, b.bcnt, b.bbase, b.bcur, b.ent);
+  });
+}
+
+// Pass 2: for each token block (outer) and vocabulary chunk (inner),
+// recompute the logits, form the logit gradient (teacher entries included)
+// and contract it into dH / dW (fp32 or bf16 per the flags).  A block's h^T
+// is made once; its dH rows are final after its last chunk, a dW chunk after
+// the last block.
 void launch_backward(Launcher& L, const Plan& P, uint32_t flags, const Inputs& in, const Bufs& b, void* dH_out,
                      void* dW_out) {
   hipStream_t s = L.s;
   using namespace kd;
   const int64_t T = P.T, H = P.H, V = P.V;
-  const int K = P.K;
   const float c = kLog2e / P.tau;
   const bool bf16 = (flags & KD_FLAG_GRAD_BF16) != 0;
   const bool acc_dh_in = (flags & KD_FLAG_ACCUMULATE_DH) != 0;
   const bool acc_dw_in = (flags & KD_FLAG_ACCUMULATE_DW) != 0;
-  // fp32 targets of the contractions
-  float* dH = dH_out ? (bf16 ? b.dhs : static_cast<float*>(dH_out)) : nullptr;
-  float* dWc_stage = dW_out && bf16 ? b.dws : nullptr;
+  const bool whole_dw = T > P.Tb;  // bf16 dW staging holds all of dW
   const int nht = (int)cdiv(H, 256);
   const int64_t Tp = align256(T);
   L.run(8, [&] {
     k_offsets<<<(unsigned)cdiv(Tp, 256), 256, 0, s>>>(b.lse2, in.mask, T, Tp, b.scal_f, b.off);
   });
-  // one token block: its h^T is made once; otherwise before each contraction
-  const bool one_block = T <= P.Tb;
-  if (dW_out && one_block) launch_transpose_h(L, P, in, b, 0, T);
-  int ci = 0;
-  for (int64_t v0 = 0; v0 < V; v0 += P.chunk_v, ++ci) {
-    const int64_t vrows = std::min<int64_t>(P.chunk_v, V - v0);
-    const int nvt_c = (int)cdiv(vrows, 256);
-    float* dW = dW_out ? (bf16 ? dWc_stage : static_cast<float*>(dW_out) + v0 * H) : nullptr;
-    int bi = 0;
-    for (int64_t t0 = 0; t0 < T; t0 += P.Tb, ++bi) {
-      const int64_t rows = std::min<int64_t>(P.Tb, T - t0);
-      const int ntt = (int)cdiv(rows, 256);
+  launch_buckets(L, P, in, b);
+  int bi = 0;
+  for (int64_t t0 = 0; t0 < T; t0 += P.Tb, ++bi) {
+    const int64_t rows = std::min<int64_t>(P.Tb, T - t0);
+    const int ntt = (int)cdiv(rows, 256);
+    // fp32 target of this block's dH rows
+    float* dH = dH_out ? (bf16 ? b.dhs : static_cast<float*>(dH_out) + t0 * H) : nullptr;
+    if (dW_out) launch_transpose_h(L, P, in, b, t0, rows);
+    int ci = 0;
+    for (int64_t v0 = 0; v0 < V; v0 += P.chunk_v, ++ci) {
+      const int64_t vrows = std::min<int64_t>(P.chunk_v, V - v0);
+      const int nvt_c = (int)cdiv(vrows, 256);
+      float* dW = dW_out ? (bf16 ? (whole_dw ? b.dws + v0 * H : b.dws) : static_cast<float*>(dW_out) + v0 * H)
+                         : nullptr;
       Pass2Args a{};
       a.W = in.W + v0 * H;
       a.h = in.h + t0 * H;
@@ -399,20 +443,20 @@ void launch_backward(Launcher& L, const Plan& P, uint32_t flags, const Inputs& i
       a.total = ntt * nvt_c;
       a.ldg = P.chunk_v;
       a.c = c;
+      a.bstart = b.bcnt;
+      a.bbase = b.bbase;
+      a.ent = b.ent;
+      a.ldk = P.ldk;
+      a.gtt0 = (int)(t0 / 256);
+      a.gvt0 = (int)(v0 / 256);
       const int grid = (int)(cdiv(a.total, 8) * 8);
       L.run(5, [&] { k_pass2<<<grid, 256, 0, s>>>(a); });
-      L.run(6, [&] {
-        k_fixup<<<(unsigned)cdiv(rows * K, 256), 256, 0, s>>>(in.idx + t0 * K, b.s + t0 * K, b.pm + t0 * K,
-                                                              b.lse2 + t0, in.mask ? in.mask + t0 : nullptr, b.scal_f,
-                                                              rows, K, v0, vrows, c, b.G, P.chunk_v);
-      });
-      if (dW_out && !one_block) launch_transpose_h(L, P, in, b, t0, rows);
       BwdArgs g{};
       g.W = in.W + v0 * H;
       g.hT = b.hT;
       g.ldt = P.Tb;
       g.G = b.G;
-      g.dH = dH ? dH + t0 * H : nullptr;
+      g.dH = dH;
       g.dW = dW;
       g.vrows = vrows;
       g.H = H;
@@ -434,17 +478,22 @@ void launch_backward(Launcher& L, const Plan& P, uint32_t flags, const Inputs& i
       g.acc_dh = ci > 0 || (acc_dh_in && !bf16);
       g.acc_dw = bi > 0 || (acc_dw_in && !bf16);
       L.run(7, [&] { k_bwd<<<g.ndh_pad + g.ndw_pad, 256, 0, s>>>(g); });
+      if (dW_out && bf16 && !whole_dw) {
+        const int64_t n = vrows * H;
+        uint16_t* dst = static_cast<uint16_t*>(dW_out) + v0 * H;
+        L.run(8, [&] { k_to_bf16<<<grid_fill(n / 4, 256), 256, 0, s>>>(b.dws, dst, n, acc_dw_in ? 1 : 0); });
+      }
     }
-    if (dWc_stage) {
-      const int64_t n = vrows * H;
-      uint16_t* dst = static_cast<uint16_t*>(dW_out) + v0 * H;
-      L.run(8, [&] { k_to_bf16<<<grid_fill(n / 4, 256), 256, 0, s>>>(dWc_stage, dst, n, acc_dw_in ? 1 : 0); });
+    if (dH_out && bf16) {
+      const int64_t n = rows * H;
+      uint16_t* dst = static_cast<uint16_t*>(dH_out) + t0 * H;
+      L.run(8, [&] { k_to_bf16<<<grid_fill(n / 4, 256), 256, 0, s>>>(b.dhs, dst, n, acc_dh_in ? 1 : 0); });
     }
   }
-  if (dH_out && bf16) {
-    const int64_t n = T * H;
+  if (dW_out && bf16 && whole_dw) {
+    const int64_t n = V * H;
     L.run(8, [&] {
-      k_to_bf16<<<grid_fill(n / 4, 256), 256, 0, s>>>(b.dhs, static_cast<uint16_t*>(dH_out), n, acc_dh_in ? 1 : 0);
+      k_to_bf16<<<grid_fill(n / 4, 256), 256, 0, s>>>(b.dws, static_cast<uint16_t*>(dW_out), n, acc_dw_in ? 1 : 0);
     });
   }
 }

@@ -458,6 +458,104 @@ __global__ void __launch_bounds__(1024) k_sum(const double* __restrict__ bsum, i
   if (threadIdx.x == 0) loss[0] = (float)(red[0] * (double)scal_f[1]);
 }
 
+// --------------------------------------------- teacher entries by tile
+// The cached teacher entries of kept tokens, grouped by the (token tile,
+// vocabulary tile) of 256 x 256 they fall in (the per-chunk bucketing of
+// the teacher ids), each carrying its final logit-gradient value
+// bf16(coef * (q - mass)) with q = 2^(c s - lse2) from the gathered student
+// logit: the pass-2 workgroup of that tile writes them into its staged tile.
+// Bucket (tt, vt) is slot tt * ldk + vt, ldk = nvt + 1; after the scans slot
+// (tt, vt) holds the bucket's start relative to the token tile's first
+// entry, slot (tt, nvt) the token tile's count, and base[tt] the token
+// tile's first entry.  An entry is (t & 255) | (v & 255) << 8 | bits << 16.
+__global__ void k_bucket_count(const int32_t* __restrict__ idx, const uint8_t* __restrict__ mask, int64_t T, int K,
+                               int64_t V, int ldk, uint32_t* __restrict__ cnt) {
+  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (i >= T * K) return;
+  const int64_t t = i / K;
+  if (mask && mask[t] == 0) return;
+  const int32_t v = idx[i];
+  if (v < 0 || (int64_t)v >= V) return;
+  atomicAdd(cnt + (t >> 8) * ldk + (v >> 8), 1u);
+}
+
+// Exclusive scan of n counts in place, one workgroup per row of `data`
+// (stride ld); data[n] of the row receives the row's total.  Thread j
+// scans a contiguous share of the row.
+__global__ void __launch_bounds__(1024) k_scan_rows(uint32_t* __restrict__ data, int n, int64_t ld) {
+  __shared__ uint32_t part[1024];
+  uint32_t* row = data + (int64_t)blockIdx.x * ld;
+  const int per = (n + 1023) / 1024;
+  const int j = threadIdx.x;
+  const int b0 = min(n, j * per), b1 = min(n, b0 + per);
+  uint32_t sum = 0;
+  for (int i = b0; i < b1; ++i) sum += row[i];
+  part[j] = sum;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {  // inclusive scan of the shares
+    const uint32_t v = j >= o ? part[j - o] : 0u;
+    __syncthreads();
+    part[j] += v;
+    __syncthreads();
+  }
+  uint32_t run = j ? part[j - 1] : 0u;
+  for (int i = b0; i < b1; ++i) {
+    const uint32_t c = row[i];
+    row[i] = run;
+    run += c;
+  }
+  if (j == 1023) row[n] = part[1023];
+}
+
+// base[tt] = first entry of token tile tt (exclusive scan of the tile
+// totals that k_scan_rows left in slot nvt of each row); one workgroup.
+__global__ void __launch_bounds__(1024) k_scan_tiles(const uint32_t* __restrict__ start, int ntt, int ldk, int nvt,
+                                                      uint32_t* __restrict__ base) {
+  __shared__ uint32_t part[1024];
+  const int per = (ntt + 1023) / 1024;
+  const int j = threadIdx.x;
+  const int b0 = min(ntt, j * per), b1 = min(ntt, b0 + per);
+  uint32_t sum = 0;
+  for (int i = b0; i < b1; ++i) sum += start[(int64_t)i * ldk + nvt];
+  part[j] = sum;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {
+    const uint32_t v = j >= o ? part[j - o] : 0u;
+    __syncthreads();
+    part[j] += v;
+    __syncthreads();
+  }
+  uint32_t run = j ? part[j - 1] : 0u;
+  for (int i = b0; i < b1; ++i) {
+    base[i] = run;
+    run += start[(int64_t)i * ldk + nvt];
+  }
+}
+
+// Places every kept entry in its bucket (order inside a bucket is free: two
+// entries of one (t, v), duplicate ids, carry the same value) with its
+// gradient value, the same arithmetic as the dense fixup of the
+// sequence-chunk schedule (k_fixup).
+__global__ void k_bucket_fill(const int32_t* __restrict__ idx, const float* __restrict__ s,
+                              const float* __restrict__ pm, const float* __restrict__ lse2,
+                              const uint8_t* __restrict__ mask, const float* __restrict__ scal_f, int64_t T, int K,
+                              int64_t V, float c, int ldk, const uint32_t* __restrict__ start,
+                              const uint32_t* __restrict__ base, uint32_t* __restrict__ cur,
+                              uint32_t* __restrict__ ent) {
+  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (i >= T * K) return;
+  const int64_t t = i / K;
+  if (mask && mask[t] == 0) return;
+  const int32_t v = idx[i];
+  if (v < 0 || (int64_t)v >= V) return;
+  const int64_t key = (t >> 8) * ldk + (v >> 8);
+  const uint32_t pos = base[t >> 8] + start[key] + atomicAdd(cur + key, 1u);
+  const float q = fast_exp2(fmaf(s[i], c, -lse2[t]));
+  const float g = scal_f[0] * (q - pm[i]);
+  const uint32_t bits = __builtin_bit_cast(uint16_t, (__bf16)g);
+  ent[pos] = (uint32_t)(t & 255) | ((uint32_t)(v & 255) << 8) | (bits << 16);
+}
+
 // ----------------------------------------------------------------- pass 2
 // One (token block, vocabulary chunk): G[t, v] = coef_t 2^(c S[t,v] - lse2[t])
 // in bf16 for every (t, v) of the padded tile grid (zero outside the valid
@@ -485,6 +583,13 @@ struct Pass2Args {
   int64_t vrows, H, rows; // valid vocabulary rows in chunk / tokens in block
   int ntt, nvt, gt, gv, total, ldg;  // gv > 0: group vocabulary tiles instead
   float c;
+  // teacher entries by tile (k_bucket_*; nullable: none written): bucket
+  // starts [*, ldk], token-tile bases, entries; global tile index of this
+  // launch's first token / vocabulary tile
+  const uint32_t* bstart;
+  const uint32_t* bbase;
+  const uint32_t* ent;
+  int ldk, gtt0, gvt0;
 };
 
 __global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) k_pass2(Pass2Args a) {
@@ -512,8 +617,20 @@ __global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 
                                              0);
   }
   const float cs = a.scal_f[0];
+  // this tile's teacher entries: [e0, e1) of a.ent
+  uint32_t e0 = 0, e1 = 0;
+  if (a.ent) {
+    const int gtt = a.gtt0 + tt;
+    const int64_t key = (int64_t)gtt * a.ldk + a.gvt0 + vt;
+    const uint32_t bb = a.bbase[gtt];
+    e0 = bb + a.bstart[key];
+    e1 = bb + a.bstart[key + 1];
+  }
   f32x16 acc[4][4];
   gemm_tile<4, 4>(la, lb, (int)(a.H / kBK), st, acc);
+  const int tid = threadIdx.x;
+  // first entries now: their latency hides under the exponentials below
+  const uint32_t ent0 = e0 + (uint32_t)tid < e1 ? a.ent[e0 + tid] : 0u;
   const uint32_t sgn = cs < 0.f ? 0x80008000u : 0u;  // sign bits of a negative coefficient
   // The bf16 tile goes through LDS (the four stages, 4 x 32 KiB, are free
   // after gemm_tile; 64 token rows each) as [256 tokens][256 vocab] rows of
@@ -544,10 +661,19 @@ __global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 
       }
   }
   __syncthreads();
+  // the teacher entries replace the dense values at their (token, id)
+  if (e1 > e0) {
+    auto put = [&](uint32_t x) {
+      const int tl = x & 255, vr = (x >> 8) & 255;
+      row(tl)[((vr >> 3) ^ (tl & 31)) * 8 + (vr & 7)] = (uint16_t)(x >> 16);
+    };
+    if (e0 + (uint32_t)tid < e1) put(ent0);
+    for (uint32_t e = e0 + 256 + tid; e < e1; e += 256) put(a.ent[e]);
+    __syncthreads();
+  }
   // vocabulary columns past the chunk's valid rows leave as zeros (only in
   // the chunk's last tile)
   const int lim = (int)min<int64_t>(256, a.vrows - (int64_t)vt * 256);
-  const int tid = threadIdx.x;
   if (lim == 256) {
 #pragma unroll 4
     for (int e = tid; e < 256 * 32; e += 256) {
@@ -571,7 +697,9 @@ __global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 
 }
 
 // At each cached teacher id inside this (block, chunk), replace the dense
-// value by coef * (q - mass) with q = 2^(c s - lse2) from the gathered logit.
+// value by coef * (q - mass) with q = 2^(c s - lse2) from the gathered logit
+// (the sequence-chunk schedule; the recompute schedule's pass 2 writes the
+// bucketed entries itself).
 __global__ void k_fixup(const int32_t* __restrict__ idx, const float* __restrict__ s, const float* __restrict__ pm,
                         const float* __restrict__ lse2, const uint8_t* __restrict__ mask,
                         const float* __restrict__ scal_f, int64_t rows, int K, int64_t v0, int64_t vrows, float c,

@@ -63,8 +63,10 @@ typedef enum kd_status {
 #define KD_FLAG_ACCUMULATE_DH 2u
 #define KD_FLAG_ACCUMULATE_DW 4u
 /* dH and dW are bf16 (bit patterns) instead of fp32.  The contractions still
- * accumulate in fp32 inside the workspace (dH [T,H] and one chunk of dW,
- * [chunk_v,H]) and each output element is rounded to bf16 once (to nearest
+ * accumulate in fp32 inside the workspace (one token block of dH,
+ * [block_t,H], and one chunk of dW, [chunk_v,H], or all of dW [V,H] when T
+ * exceeds one token block; with KD_FLAG_SEQ_CHUNK all of dH [T,H]) and each
+ * output element is rounded to bf16 once (to nearest
  * even), after its last contribution (with an accumulate flag: once, after
  * adding the previous bf16 value in fp32). */
 #define KD_FLAG_GRAD_BF16 8u

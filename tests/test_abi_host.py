@@ -60,7 +60,10 @@ def test_workspace_plan():
     _, b = _ws(131072, 2880, 201088, 64)
     _, c = _ws(262144, 2880, 201088, 64)
     assert abs((c - b) - 2 * (b - a)) <= 4096
-    assert (c - b) / 131072 < 1024  # bytes per token of workspace, far below 2V = 402 KB
+    # bytes per token of workspace (teacher probabilities, merged mass, gathered
+    # logit and bucketed entry: 4 K floats, plus a few per-token scalars), far
+    # below one bf16 logit row (2V = 402 KB)
+    assert (c - b) / 131072 < 16 * 64 + 256
 
 
 @pytest.mark.parametrize("args,code", [
@@ -153,9 +156,13 @@ def test_split_entry_point_sizes():
     assert code == 0
     code, fwd = _size(L.kd_topk_kl_fwd_workspace_size, T, H, V, K)
     assert code == 0
-    # the forward needs no gradient buffer (4096 x 12288 bf16), no h^T (2880 x 4096 bf16)
-    # and no per-token pass-2 offsets (4096 fp32)
-    assert full - fwd == 4096 * 12288 * 2 + H * 4096 * 2 + 4 * 4096
+    # the forward needs no gradient buffer (4096 x 12288 bf16), no h^T (2880 x 4096 bf16),
+    # no per-token pass-2 offsets (4096 fp32) and no bucketed teacher entries (counts and
+    # cursors per (token tile, vocabulary tile), token-tile bases, one word per entry)
+    r256 = lambda x: (x + 255) // 256 * 256
+    nkeys = (T // 256) * ((V + 255) // 256 + 1)
+    assert full - fwd == (4096 * 12288 * 2 + H * 4096 * 2 + 4 * 4096 + r256(8 * nkeys) + r256(4 * (T // 256) + 4)
+                          + 4 * T * K)
     code, saved = _size(L.kd_topk_kl_saved_size, T, H, V, K)
     assert code == 0
     # log-sum-exp [T] and the gathered logits [T, K], fp32, 256-byte aligned pieces
