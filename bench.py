@@ -10,8 +10,10 @@ schedule (stored block logits instead of the pass-2 recompute), and
 "logits_variant" the forward-chunked KL on the batch's materialised logits.
 
 Other modes (not the benchmark line):
-  --copy-probe      a plain device copy of known size, to calibrate rocprofv3
-                    FETCH_SIZE / WRITE_SIZE against the algorithmic bytes
+  --copy-probe      a plain device copy of known size, to check rocprofv3
+                    byte counts against the algorithmic bytes
+  --summarize-counters DIR WORKLOAD OUT
+                    per-kernel L2-to-fabric bytes from rocprofv3 --pmc passes
   --sweep           tokens/s and peak memory over T in {4096 ... 262144}
                     (the default run already carries them in "scaling")
 
@@ -38,8 +40,10 @@ if ROOT not in sys.path:
 METRIC = "tokens/s fwd+bwd fused chunked KL (H=2880,V=201088,K=64); MFMA util; peak mem"
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
-PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "bwd_traffic_gptoss.json")
-# the sources k_bwd is built and launched from (the traffic summary is its)
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "bwd_pass2_traffic_gptoss.json")
+ROOFLINE_KERNEL = "k_bwd_pass2"
+# the sources the roofline kernel is built and launched from (the traffic
+# summary is attached to them)
 KERNEL_SOURCES = [os.path.join(ROOT, "chunked_kl_loss_02_amd", "csrc", f)
                   for f in ("kd_common.hpp", "kd_gemm.hpp", "kd_kernels.hpp", "kd_host.hip")]
 
@@ -95,17 +99,36 @@ def cpu_baseline(x, tau, rows: int, seed: int = 0):
             "seconds": dt}
 
 
-def load_traffic(launch_flops):
-    """HBM bytes per bwd launch from the committed rocprofv3 counter summary,
-    if it was taken on the current kernel sources; else None."""
+def load_traffic():
+    """(bytes per launch, what they count) of the roofline kernel from the
+    committed rocprofv3 counter summary, if it was taken on the current
+    kernel sources; else (None, reason)."""
     try:
         with open(PROFILE_TRAFFIC) as f:
             d = json.load(f)
     except (OSError, ValueError):
-        return None
+        return None, "no counter summary"
     if d.get("kernel_source_hash") != kernel_source_hash():
-        return None
-    return d.get("hbm_bytes_per_launch")
+        return None, "counter summary taken on other kernel sources"
+    k = d["kernels"].get(ROOFLINE_KERNEL)
+    if not k:
+        return None, "roofline kernel missing from the counter summary"
+    return k["read_bytes"] + k["write_bytes"], d["counts"]
+
+
+def merged_flops(T, H, V, K, tau):
+    """MFMA flops of the k_bwd_pass2 launches of one call and their number:
+    launch i holds unit i's dH and dW contractions (4 H rows_i vrows_i) and
+    unit i+1's pass-2 recompute (2 H rows_{i+1} vrows_{i+1}); units are
+    (token block, vocabulary chunk) pairs in the library's order, the last
+    unit's contractions launch alone (k_bwd)."""
+    import chunked_kl_loss_02_amd as kd
+    bt, cv, nbuf = kd.tiling(T, H, V, K, tau)
+    units = [(min(bt, T - t0), min(cv, V - v0)) for t0 in range(0, T, bt) for v0 in range(0, V, cv)]
+    if nbuf < 2:
+        return 0.0, 0
+    f = sum(4.0 * H * r * v + 2.0 * H * units[i + 1][0] * units[i + 1][1] for i, (r, v) in enumerate(units[:-1]))
+    return f, len(units) - 1
 
 
 def run_seq_chunk(args, wl, x):
@@ -243,16 +266,16 @@ def run_one(args, wl):
     base_alloc = torch.cuda.memory_allocated(dev)
     torch.cuda.reset_peak_memory_stats(dev)
     # the timed region: events only around the roofline kernel's launches
-    dt, pk = timed_steps(step, args.steps, ["bwd"])
+    dt, pk = timed_steps(step, args.steps, ["bwd_pass2"])
     peak = torch.cuda.max_memory_allocated(dev)
     loss = outs[0].item()
     ms_step = dt * 1e3 / args.steps
-    bwd_ms, bwd_n = pk["bwd"]
+    mg_ms, mg_n = pk["bwd_pass2"]
     # per-kernel breakdown: the same steps again, events around every launch
     dt_all, per_kernel = timed_steps(step, args.steps)
-    bwd_flops_total = 4.0 * T * H * V * args.steps       # dH + dW contractions
-    achieved = bwd_flops_total / (bwd_ms * 1e-3) / 1e12 if bwd_ms > 0 else 0.0
-    traffic = load_traffic(bwd_flops_total / max(bwd_n, 1))
+    mg_flops, mg_launches = merged_flops(T, H, V, K, tau)
+    achieved = mg_flops * args.steps / (mg_ms * 1e-3) / 1e12 if mg_ms > 0 else 0.0
+    traffic, traffic_kind = load_traffic()
     res = {
         "metric": METRIC,
         "value": T * args.steps / dt,
@@ -268,10 +291,13 @@ def run_one(args, wl):
         "data": "synthetic (seeded h~N(0,1), W~2N(0,1)/sqrt(H), teacher top-K of noisy student logits)",
         "config": {"workload": wl.name, "T": T, "H": H, "V": V, "K": K, "tau": tau, "mask": wl.mask,
                    "seq_len": T, "global_batch": 1, "parallelism": "none (1 GPU)"},
-        "roofline": {"bound": "mfma", "kernel": "k_bwd (dH = G W_c and dW_c = G^T h, bf16 MFMA)",
+        "roofline": {"bound": "mfma",
+                     "kernel": "k_bwd_pass2 (dH = G W_c and dW_c = G^T h of one (block, chunk) unit and the next "
+                               "unit's pass-2 recompute, bf16 MFMA)",
                      "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic,
-                     "avg_launch_ms": bwd_ms / max(bwd_n, 1), "launches": bwd_n},
+                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic, "traffic_kind": traffic_kind,
+                     "flops_per_launch": mg_flops / max(mg_launches, 1),
+                     "avg_launch_ms": mg_ms / max(mg_n, 1), "launches": mg_n},
         "tflops_total": flops_per_token(H, V) * T * args.steps / dt / 1e12,
         "mfma_util_total": flops_per_token(H, V) * T * args.steps / dt / 1e12 / PEAK_BF16_TFLOPS,
         "per_kernel_ms_per_step": {k: v[0] / args.steps for k, v in per_kernel.items() if v[1]},
@@ -315,16 +341,17 @@ def run_scaling_point(args, wl, steps, warmup):
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    dt, pk = timed_steps(step, steps, ["bwd"])
+    dt, pk = timed_steps(step, steps, ["bwd_pass2"])
     peak = torch.cuda.max_memory_allocated(dev)
     inputs = sum(t.numel() * t.element_size() for t in x.values())
-    bwd_ms, bwd_n = pk["bwd"]
+    mg_ms, _ = pk["bwd_pass2"]
+    mg_flops, _ = merged_flops(T, H, V, K, tau)
     flops = flops_per_token(H, V) * T
     res = {"workload": wl.name, "T": T, "H": H, "V": V, "K": K, "tau": tau, "mask": wl.mask,
            "kept_tokens": int(x["mask"].sum().item()), "steps": steps, "warmup": warmup,
            "value": T * steps / dt, "unit": "tokens/s", "ms_per_step": dt * 1e3 / steps,
            "tflops": flops * steps / dt / 1e12, "mfma_frac": flops * steps / dt / 1e12 / PEAK_BF16_TFLOPS,
-           "bwd_tflops": 4.0 * T * H * V * steps / (bwd_ms * 1e-3) / 1e12 if bwd_ms > 0 else 0.0,
+           "bwd_pass2_tflops": mg_flops * steps / (mg_ms * 1e-3) / 1e12 if mg_ms > 0 else 0.0,
            "peak_mem_bytes": int(peak - base + inputs), "workspace_bytes": int(ws_bytes),
            "naive_logits_bytes": naive_logit_bytes(T, V), "loss": outs[0].item()}
     del x, ws, outs
@@ -375,6 +402,52 @@ def cpu_tiny_full(seconds=3.0):
     return res
 
 
+def summarize_counters(pmc_dir, workload, out_json):
+    """Per-kernel bytes per dispatch from four rocprofv3 --pmc passes over the
+    same program (directories pmc_dir/{A,B,C,D}, files <workload>_counter_collection.csv):
+      A  TCC_EA0_RDREQ_32B_sum TCC_EA0_RDREQ_64B_sum TCC_EA0_RDREQ_128B_sum TCC_EA0_RDREQ_sum
+      B  TCC_EA0_WRREQ_sum TCC_EA0_WRREQ_64B_sum TCC_EA0_RDREQ_DRAM_32B_sum TCC_EA0_WRREQ_DRAM_sum
+      C  FETCH_SIZE        D  WRITE_SIZE
+    read = 32 n32 + 64 n64 + 128 n128 (the L2's read requests to the fabric by
+    size), write = 32 (nW - nW64) + 64 nW64; FETCH_SIZE and WRITE_SIZE are
+    kept beside them as a cross-check.  These count bytes between the L2
+    and the memory fabric: last-level (Infinity) cache hits are included,
+    so they bound HBM traffic from above."""
+    import csv
+    import collections
+    def load(pas):
+        path = os.path.join(pmc_dir, pas, f"{workload}_counter_collection.csv")
+        acc = collections.defaultdict(lambda: collections.defaultdict(float))
+        disp = collections.defaultdict(set)
+        for r in csv.DictReader(open(path)):
+            m = re.search(r"\bkd::(k_\w+)", r["Kernel_Name"])
+            name = m.group(1) if m else "other:" + r["Kernel_Name"][:40]
+            acc[name][r["Counter_Name"]] += float(r["Counter_Value"])
+            disp[name].add(r["Dispatch_Id"])
+        return {k: ({c: v / len(disp[k]) for c, v in acc[k].items()}, len(disp[k])) for k in acc}
+    A, B, C, D = (load(p) for p in "ABCD")
+    kernels = {}
+    for k, (a, n) in A.items():
+        if k.startswith("other:"):
+            continue
+        b, c, d = B[k][0], C.get(k, ({}, 0))[0], D.get(k, ({}, 0))[0]
+        rd = 32 * a["TCC_EA0_RDREQ_32B_sum"] + 64 * a["TCC_EA0_RDREQ_64B_sum"] + 128 * a["TCC_EA0_RDREQ_128B_sum"]
+        wr = 32 * (b["TCC_EA0_WRREQ_sum"] - b["TCC_EA0_WRREQ_64B_sum"]) + 64 * b["TCC_EA0_WRREQ_64B_sum"]
+        kernels[k] = {"dispatches": n, "read_bytes": rd, "write_bytes": wr,
+                      "dram_read_bytes": 32 * b["TCC_EA0_RDREQ_DRAM_32B_sum"],
+                      "fetch_size_bytes": 1024 * c.get("FETCH_SIZE", 0.0),
+                      "write_size_bytes": 1024 * d.get("WRITE_SIZE", 0.0)}
+    out = {"workload": workload, "kernel_source_hash": kernel_source_hash(),
+           "counts": "L2-to-fabric bytes per dispatch (TCC_EA0 read requests by size, write requests); "
+                     "last-level (Infinity) cache hits included, so an upper bound on HBM bytes",
+           "kernels": kernels}
+    with open(out_json, "w") as f:
+        json.dump(out, f, indent=1, sort_keys=True)
+    for k, v in sorted(kernels.items(), key=lambda kv: -kv[1]["read_bytes"]):
+        print(f"{k:22s} n={v['dispatches']:5d} read {v['read_bytes'] / 1e6:10.1f} MB  write {v['write_bytes'] / 1e6:9.1f} MB"
+              f"  (FETCH_SIZE {v['fetch_size_bytes'] / 1e6:9.1f} MB, WRITE_SIZE {v['write_size_bytes'] / 1e6:9.1f} MB)")
+
+
 def copy_probe(nbytes=1 << 30, reps=5):
     """Plain device-to-device copy of nbytes, for counter calibration."""
     import torch
@@ -400,6 +473,8 @@ def main():
     ap.add_argument("--no-variants", action="store_true", help="skip the logits / top-K variant lines")
     ap.add_argument("--cpu-rows", type=int, default=2048)
     ap.add_argument("--no-scaling", action="store_true", help="skip the long / qwen / T-sweep lines")
+    ap.add_argument("--summarize-counters", nargs=3, metavar=("PMC_DIR", "WORKLOAD", "OUT_JSON"),
+                    help="per-kernel L2-to-fabric bytes from four rocprofv3 --pmc passes (see summarize_counters)")
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--sweep", action="store_true")
     args = ap.parse_args()
@@ -409,6 +484,9 @@ def main():
         sys.exit(2)
     if args.copy_probe:
         copy_probe()
+        return
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters)
         return
     import synth
     if args.sweep:

@@ -11,7 +11,7 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["fwd_bwd", "fwd_bwd_noalloc", "NOALLOC_SCRATCH_BYTES", "fwd", "bwd", "topk_kl_loss", "kl_logits", "logits_workspace_size", "KdLogitsProblem",
+__all__ = ["fwd_bwd", "fwd_bwd_noalloc", "tiling", "NOALLOC_SCRATCH_BYTES", "fwd", "bwd", "topk_kl_loss", "kl_logits", "logits_workspace_size", "KdLogitsProblem",
            "topk_select", "KdTopkProblem", "TopKKLLoss", "workspace_size", "fwd_workspace_size",
            "saved_size", "lse", "saved_lse", "KdProblem", "library_path", "lib", "timing_enable",
            "timing_collect", "KERNEL_CLASSES", "KD_FLAG_VALIDATE", "KD_FLAG_ACCUMULATE_DH",
@@ -25,10 +25,11 @@ KD_FLAG_ACCUMULATE_DH = 2
 KD_FLAG_ACCUMULATE_DW = 4
 KD_FLAG_GRAD_BF16 = 8
 KD_FLAG_SEQ_CHUNK = 16
-ABI_VERSION = 4
+ABI_VERSION = 5
 KD_FLAG_LOGITS_F32 = 32
 NOALLOC_SCRATCH_BYTES = 128 << 20  # KD_NOALLOC_SCRATCH_BYTES
-KERNEL_CLASSES = ("teacher", "gather", "pass1", "lse", "loss", "pass2", "fixup", "bwd", "other", "logits", "topk")
+KERNEL_CLASSES = ("teacher", "gather", "pass1", "lse", "loss", "pass2", "fixup", "bwd", "other", "logits", "topk",
+                  "bwd_pass2")
 _STATUS = {0: "KD_OK", 1: "KD_ERR_ARG", 2: "KD_ERR_UNSUPPORTED", 3: "KD_ERR_WORKSPACE",
            4: "KD_ERR_INDEX", 5: "KD_ERR_NONFINITE", 6: "KD_ERR_HIP"}
 
@@ -76,6 +77,9 @@ def lib():
     P = ctypes.POINTER(KdProblem)
     L.kd_topk_kl_workspace_size.argtypes = [P, ctypes.POINTER(sz)]
     L.kd_topk_kl_workspace_size.restype = ctypes.c_int
+    L.kd_topk_kl_tiling.argtypes = [P, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64),
+                                    ctypes.POINTER(ctypes.c_int32)]
+    L.kd_topk_kl_tiling.restype = ctypes.c_int
     L.kd_topk_kl_fwd_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.kd_topk_kl_fwd_bwd.restype = ctypes.c_int
     L.kd_topk_kl_fwd_bwd_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
@@ -132,6 +136,16 @@ def workspace_size(T, H, V, K, tau=1.0, chunk_v=0, block_t=0, flags=0, seq_chunk
     """Workspace bytes of fwd_bwd / bwd."""
     flags |= KD_FLAG_SEQ_CHUNK if seq_chunk else 0
     return _size(lib().kd_topk_kl_workspace_size, problem(T, H, V, K, tau, chunk_v, block_t, flags=flags))
+
+
+def tiling(T, H, V, K, tau=1.0, chunk_v=0, block_t=0, flags=0, seq_chunk=False):
+    """(tokens per block, vocabulary rows per chunk, gradient buffers) that
+    fwd_bwd / bwd use for this problem."""
+    flags |= KD_FLAG_SEQ_CHUNK if seq_chunk else 0
+    bt, cv, nb = ctypes.c_int64(0), ctypes.c_int64(0), ctypes.c_int32(0)
+    prob = problem(T, H, V, K, tau, chunk_v, block_t, flags=flags)
+    _raise(lib().kd_topk_kl_tiling(ctypes.byref(prob), ctypes.byref(bt), ctypes.byref(cv), ctypes.byref(nb)))
+    return bt.value, cv.value, nb.value
 
 
 def fwd_workspace_size(T, H, V, K, tau=1.0, chunk_v=0, block_t=0) -> int:

@@ -278,7 +278,7 @@ __device__ __forceinline__ void gemm_tile(LA& la, LB& lb, int nk, const Stages& 
   __shared__ __attribute__((aligned(16))) uint16_t name##_a1[(BM) * kBK]; \
   __shared__ __attribute__((aligned(16))) uint16_t name##_b0[(BN) * kBK]; \
   __shared__ __attribute__((aligned(16))) uint16_t name##_b1[(BN) * kBK]; \
-  const Stages name{name##_a0, name##_a1, name##_b0, name##_b1}
+  Stages name{name##_a0, name##_a1, name##_b0, name##_b1}
 
 // Position of accumulator element e of subtile (i, j) for this lane, relative
 // to the wave's block: row (M) = 32 i + 8 (e >> 2) + 4 (lane >> 5) + (e & 3),

@@ -49,6 +49,8 @@ struct Plan {
   int gm_dh, gm_dw;  // hidden-tile group sizes of the gradient contractions
   int64_t ldp;       // leading dim of the pass-1 partials
   int64_t grows;     // rows of the gradient buffer
+  int64_t nunits;    // (token block, vocabulary chunk) units of the gradient pass
+  int ngbuf;         // gradient buffers (2: alternating between units)
   // workspace offsets (bytes); o_G, o_dhs, o_dws are meaningful only in a
   // plan made with the gradient pass (o_dhs / o_dws: fp32 staging of bf16
   // gradient outputs)
@@ -105,7 +107,7 @@ kd_status check(const kd_problem* p) {
 
 // Workspace plan.  with_grad: room for the gradient pass (the bf16 gradient
 // tile buffer, and fp32 staging when the gradient outputs are bf16).
-Plan make_plan(const kd_problem* p, bool with_grad = true) {
+Plan make_plan(const kd_problem* p, bool with_grad = true, bool one_gbuf = false) {
   Plan P{};
   P.T = p->T;
   P.H = p->H;
@@ -134,7 +136,12 @@ Plan make_plan(const kd_problem* p, bool with_grad = true) {
   const int64_t Tp = align256(P.T);
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t r = o; o += (bytes + 255) & ~size_t(255); return r; };
-  P.o_G = with_grad ? take((size_t)P.grows * P.chunk_v * 2) : 0;
+  // the recompute schedule alternates two gradient buffers when a call has
+  // several (block, chunk) units (the next unit's pass 2 runs beside the
+  // current unit's contractions)
+  P.nunits = cdiv(P.T, P.Tb) * cdiv(P.V, P.chunk_v);
+  P.ngbuf = !P.seq && !one_gbuf && P.nunits > 1 ? 2 : 1;
+  P.o_G = with_grad ? take((size_t)P.ngbuf * P.grows * P.chunk_v * 2) : 0;
   P.o_hT = with_grad ? take((size_t)P.H * P.Tb * 2) : 0;
   P.o_off = with_grad ? take((size_t)Tp * 4) : 0;
   P.ntt_all = (int)cdiv(P.T, 256);
@@ -174,7 +181,7 @@ struct TimedLaunch {
 };
 bool g_timing = false;
 uint32_t g_timing_mask = ~0u;
-constexpr int kTimingClasses = 11;
+constexpr int kTimingClasses = 12;
 std::vector<TimedLaunch> g_launches;
 std::vector<hipEvent_t> g_pool;
 
@@ -395,9 +402,11 @@ void launch_buckets(Launcher& L, const Plan& P, const Inputs& in, const Bufs& b)
 
 // Pass 2: for each token block (outer) and vocabulary chunk (inner),
 // recompute the logits, form the logit gradient (teacher entries included)
-// and contract it into dH / dW (fp32 or bf16 per the flags).  A block's h^T
-// is made once; its dH rows are final after its last chunk, a dW chunk after
-// the last block.
+// and contract it into dH / dW (fp32 or bf16 per the flags).  Unit i's
+// contractions and unit i + 1's pass 2 share one launch (k_bwd_pass2), the
+// two units' gradient tiles in alternate buffers.  A block's h^T is made
+// once; its dH rows are final after its last chunk, a dW chunk after the
+// last block.
 void launch_backward(Launcher& L, const Plan& P, uint32_t flags, const Inputs& in, const Bufs& b, void* dH_out,
                      void* dW_out) {
   hipStream_t s = L.s;
@@ -410,30 +419,41 @@ void launch_backward(Launcher& L, const Plan& P, uint32_t flags, const Inputs& i
   const bool whole_dw = T > P.Tb;  // bf16 dW staging holds all of dW
   const int nht = (int)cdiv(H, 256);
   const int64_t Tp = align256(T);
+  const size_t gbuf = (size_t)P.grows * P.chunk_v;  // elements of one gradient buffer
   L.run(8, [&] {
     k_offsets<<<(unsigned)cdiv(Tp, 256), 256, 0, s>>>(b.lse2, in.mask, T, Tp, b.scal_f, b.off);
   });
   launch_buckets(L, P, in, b);
+  struct Unit {
+    int64_t t0, rows, v0, vrows;
+    int bi, ci;
+    Pass2Args p;
+    BwdArgs g;
+  };
+  std::vector<Unit> units;
   int bi = 0;
   for (int64_t t0 = 0; t0 < T; t0 += P.Tb, ++bi) {
     const int64_t rows = std::min<int64_t>(P.Tb, T - t0);
     const int ntt = (int)cdiv(rows, 256);
-    // fp32 target of this block's dH rows
     float* dH = dH_out ? (bf16 ? b.dhs : static_cast<float*>(dH_out) + t0 * H) : nullptr;
-    if (dW_out) launch_transpose_h(L, P, in, b, t0, rows);
     int ci = 0;
     for (int64_t v0 = 0; v0 < V; v0 += P.chunk_v, ++ci) {
-      const int64_t vrows = std::min<int64_t>(P.chunk_v, V - v0);
-      const int nvt_c = (int)cdiv(vrows, 256);
-      float* dW = dW_out ? (bf16 ? (whole_dw ? b.dws + v0 * H : b.dws) : static_cast<float*>(dW_out) + v0 * H)
-                         : nullptr;
-      Pass2Args a{};
+      Unit u{};
+      u.t0 = t0;
+      u.rows = rows;
+      u.v0 = v0;
+      u.vrows = std::min<int64_t>(P.chunk_v, V - v0);
+      u.bi = bi;
+      u.ci = ci;
+      const int nvt_c = (int)cdiv(u.vrows, 256);
+      uint16_t* G = b.G + (units.size() % P.ngbuf) * gbuf;
+      Pass2Args& a = u.p;
       a.W = in.W + v0 * H;
       a.h = in.h + t0 * H;
       a.off = b.off + t0;
       a.scal_f = b.scal_f;
-      a.G = b.G;
-      a.vrows = vrows;
+      a.G = G;
+      a.vrows = u.vrows;
       a.H = H;
       a.rows = rows;
       a.ntt = ntt;
@@ -449,23 +469,21 @@ void launch_backward(Launcher& L, const Plan& P, uint32_t flags, const Inputs& i
       a.ldk = P.ldk;
       a.gtt0 = (int)(t0 / 256);
       a.gvt0 = (int)(v0 / 256);
-      const int grid = (int)(cdiv(a.total, 8) * 8);
-      L.run(5, [&] { k_pass2<<<grid, 256, 0, s>>>(a); });
-      BwdArgs g{};
+      BwdArgs& g = u.g;
       g.W = in.W + v0 * H;
       g.hT = b.hT;
       g.ldt = P.Tb;
-      g.G = b.G;
+      g.G = G;
       g.dH = dH;
-      g.dW = dW;
-      g.vrows = vrows;
+      g.dW = dW_out ? (bf16 ? (whole_dw ? b.dws + v0 * H : b.dws) : static_cast<float*>(dW_out) + v0 * H) : nullptr;
+      g.vrows = u.vrows;
       g.H = H;
       g.rows = rows;
       g.nht = nht;
       g.ntt = ntt;
       g.nvt = nvt_c;
-      g.ndh = dH ? nht * ntt : 0;
-      g.ndw = dW ? nht * nvt_c : 0;
+      g.ndh = g.dH ? nht * ntt : 0;
+      g.ndw = g.dW ? nht * nvt_c : 0;
       g.ndh_pad = (int)(cdiv(g.ndh, 8) * 8);
       g.ndw_pad = (int)(cdiv(g.ndw, 8) * 8);
       g.gm_dh = std::min(P.gm_dh, nht);
@@ -477,16 +495,37 @@ void launch_backward(Launcher& L, const Plan& P, uint32_t flags, const Inputs& i
       // in the final rounding instead)
       g.acc_dh = ci > 0 || (acc_dh_in && !bf16);
       g.acc_dw = bi > 0 || (acc_dw_in && !bf16);
-      L.run(7, [&] { k_bwd<<<g.ndh_pad + g.ndw_pad, 256, 0, s>>>(g); });
-      if (dW_out && bf16 && !whole_dw) {
-        const int64_t n = vrows * H;
-        uint16_t* dst = static_cast<uint16_t*>(dW_out) + v0 * H;
-        L.run(8, [&] { k_to_bf16<<<grid_fill(n / 4, 256), 256, 0, s>>>(b.dws, dst, n, acc_dw_in ? 1 : 0); });
-      }
+      units.push_back(u);
     }
-    if (dH_out && bf16) {
-      const int64_t n = rows * H;
-      uint16_t* dst = static_cast<uint16_t*>(dH_out) + t0 * H;
+  }
+  const int64_t nchunks = cdiv(V, P.chunk_v);
+  auto pad8 = [](int n) { return (int)(cdiv(n, 8) * 8); };
+  // one gradient buffer (the allocation-free entry point): pass 2 and the
+  // contractions of each unit in launches of their own
+  const bool merged = P.ngbuf == 2;
+  if (merged) L.run(5, [&] { k_pass2<<<pad8(units[0].p.total), 256, 0, s>>>(units[0].p); });
+  for (size_t i = 0; i < units.size(); ++i) {
+    const Unit& u = units[i];
+    if (dW_out && u.ci == 0) launch_transpose_h(L, P, in, b, u.t0, u.rows);
+    const int nb = u.g.ndh_pad + u.g.ndw_pad;
+    if (!merged) {
+      L.run(5, [&] { k_pass2<<<pad8(u.p.total), 256, 0, s>>>(u.p); });
+      L.run(7, [&] { k_bwd<<<nb, 256, 0, s>>>(u.g); });
+    } else if (i + 1 < units.size()) {
+      const Pass2Args& pn = units[i + 1].p;
+      const int p_pad = pad8(pn.total);
+      L.run(11, [&] { k_bwd_pass2<<<nb + p_pad, 256, 0, s>>>(u.g, pn, p_pad); });
+    } else {
+      L.run(7, [&] { k_bwd<<<nb, 256, 0, s>>>(u.g); });
+    }
+    if (dW_out && bf16 && !whole_dw) {
+      const int64_t n = u.vrows * H;
+      uint16_t* dst = static_cast<uint16_t*>(dW_out) + u.v0 * H;
+      L.run(8, [&] { k_to_bf16<<<grid_fill(n / 4, 256), 256, 0, s>>>(b.dws, dst, n, acc_dw_in ? 1 : 0); });
+    }
+    if (dH_out && bf16 && u.ci == nchunks - 1) {
+      const int64_t n = u.rows * H;
+      uint16_t* dst = static_cast<uint16_t*>(dH_out) + u.t0 * H;
       L.run(8, [&] { k_to_bf16<<<grid_fill(n / 4, 256), 256, 0, s>>>(b.dhs, dst, n, acc_dh_in ? 1 : 0); });
     }
   }
@@ -662,8 +701,8 @@ kd_status fwd_bwd_args(const kd_problem* p, const uint16_t* h, const uint16_t* W
 // least make_plan(p).total bytes.
 kd_status fwd_bwd_run(const kd_problem* p, const uint16_t* h, const uint16_t* W, const int32_t* teacher_idx,
                       const float* teacher_logit, const uint8_t* mask, float* loss, void* dH, void* dW,
-                      float* row_loss, void* workspace, hipStream_t stream) {
-  const Plan P = make_plan(p);
+                      float* row_loss, void* workspace, hipStream_t stream, bool one_gbuf) {
+  const Plan P = make_plan(p, true, one_gbuf);
   Launcher L{stream};
   const Inputs in{h, W, teacher_idx, teacher_logit, mask};
   const Bufs b = carve(P, workspace, true);
@@ -725,7 +764,7 @@ kd_status scratch_for(hipStream_t stream, void** out) {
 
 extern "C" {
 
-int kd_abi_version(void) { return 4; }
+int kd_abi_version(void) { return 5; }
 
 const char* kd_status_string(kd_status s) {
   switch (s) {
@@ -738,6 +777,17 @@ const char* kd_status_string(kd_status s) {
     case KD_ERR_HIP: return "HIP runtime error";
   }
   return "unknown status";
+}
+
+kd_status kd_topk_kl_tiling(const kd_problem* p, int64_t* block_t, int64_t* chunk_v, int32_t* gbufs) {
+  if (!block_t || !chunk_v || !gbufs) return KD_ERR_ARG;
+  const kd_status st = check(p);
+  if (st != KD_OK) return st;
+  const Plan P = make_plan(p);
+  *block_t = P.Tb;
+  *chunk_v = P.chunk_v;
+  *gbufs = P.ngbuf;
+  return KD_OK;
 }
 
 kd_status kd_topk_kl_workspace_size(const kd_problem* p, size_t* bytes) {
@@ -791,7 +841,7 @@ kd_status kd_topk_kl_fwd_bwd(const kd_problem* p, const uint16_t* h, const uint1
   if (misaligned(workspace, 256)) return KD_ERR_UNSUPPORTED;
   if (workspace_bytes < make_plan(p).total) return KD_ERR_WORKSPACE;
   return fwd_bwd_run(p, h, W, teacher_idx, teacher_logit, mask, loss, dH, dW, row_loss, workspace,
-                     static_cast<hipStream_t>(stream));
+                     static_cast<hipStream_t>(stream), false);
 }
 
 kd_status kd_topk_kl_fwd_bwd_noalloc(const kd_problem* p, const uint16_t* h, const uint16_t* W,
@@ -799,12 +849,12 @@ kd_status kd_topk_kl_fwd_bwd_noalloc(const kd_problem* p, const uint16_t* h, con
                                      float* loss, void* dH, void* dW, float* row_loss, void* stream) {
   kd_status st = fwd_bwd_args(p, h, W, teacher_idx, teacher_logit, loss, dH, dW, row_loss);
   if (st != KD_OK) return st;
-  if (make_plan(p).total > (size_t)KD_NOALLOC_SCRATCH_BYTES) return KD_ERR_WORKSPACE;
+  if (make_plan(p, true, true).total > (size_t)KD_NOALLOC_SCRATCH_BYTES) return KD_ERR_WORKSPACE;
   void* ws = nullptr;
   st = scratch_for(static_cast<hipStream_t>(stream), &ws);
   if (st != KD_OK) return st;
   return fwd_bwd_run(p, h, W, teacher_idx, teacher_logit, mask, loss, dH, dW, row_loss, ws,
-                     static_cast<hipStream_t>(stream));
+                     static_cast<hipStream_t>(stream), true);
 }
 
 kd_status kd_topk_kl_saved_size(const kd_problem* p, size_t* bytes) {

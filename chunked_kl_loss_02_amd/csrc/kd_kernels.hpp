@@ -592,10 +592,8 @@ struct Pass2Args {
   int ldk, gtt0, gvt0;
 };
 
-__global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) k_pass2(Pass2Args a) {
-  KD_DECLARE_STAGES(st, 256, 256);
-  const int id = xcd_remap(blockIdx.x, gridDim.x);
-  if (id >= a.total) return;
+// One pass-2 tile, work id `id` < a.total, in the four stages `st`.
+__device__ __forceinline__ void pass2_tile(const Pass2Args& a, int id, Stages st) {
   int tt, vt;
   if (a.gv > 0)
     grouped(id, a.nvt, a.ntt, a.gv, vt, tt);
@@ -694,6 +692,13 @@ __global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 
       *reinterpret_cast<u32x4*>(a.G + (int64_t)(tt * 256 + tl) * a.ldg + vt * 256 + c * 8) = v;
     }
   }
+}
+
+__global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) k_pass2(Pass2Args a) {
+  KD_DECLARE_STAGES(st, 256, 256);
+  const int id = xcd_remap(blockIdx.x, gridDim.x);
+  if (id >= a.total) return;
+  pass2_tile(a, id, st);
 }
 
 // At each cached teacher id inside this (block, chunk), replace the dense
@@ -840,9 +845,8 @@ struct BwdArgs {
 // inside each segment the 8 XCDs get contiguous work ranges (idle padding
 // workgroups exit at once).  dH tiles come first: their K loop (the chunk's
 // vocabulary) is the longer one.
-__global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) k_bwd(BwdArgs a) {
-  KD_DECLARE_STAGES(st, 256, 256);
-  const int L = blockIdx.x;
+// One gradient-contraction workgroup, linear id L of the k_bwd grid.
+__device__ __forceinline__ void bwd_tile(const BwdArgs& a, int L, Stages st) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int wm = w & 1, wn = w >> 1;
   f32x16 acc[4][4];
@@ -927,6 +931,28 @@ __global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 
       __builtin_amdgcn_wave_barrier();
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     }
+  }
+}
+
+__global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) k_bwd(BwdArgs a) {
+  KD_DECLARE_STAGES(st, 256, 256);
+  bwd_tile(a, blockIdx.x, st);
+}
+
+// The contractions of one (token block, vocabulary chunk) and the pass-2
+// tiles of the next one, into the other gradient buffer, in one launch:
+// grid = k_bwd's grid, then p_pad (a multiple of 8) pass-2 workgroups.  The
+// dH tiles (longest) are dispatched first and the short pass-2 tiles last,
+// so they fill the contractions' uneven end instead of a launch boundary.
+__global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
+k_bwd_pass2(BwdArgs g, Pass2Args p, int p_pad) {
+  KD_DECLARE_STAGES(st, 256, 256);
+  const int nb = g.ndh_pad + g.ndw_pad;
+  if ((int)blockIdx.x < nb) {
+    bwd_tile(g, blockIdx.x, st);
+  } else {
+    const int id = xcd_remap((int)blockIdx.x - nb, p_pad);
+    if (id < p.total) pass2_tile(p, id, st);
   }
 }
 

@@ -23,11 +23,13 @@
  * even) before the two gradient contractions, fp32 dH and dW.
  *
  * Memory: besides the caller's inputs and outputs the library touches only
- * the caller's workspace (see kd_topk_kl_workspace_size): a fixed
- * block_t x chunk_v bf16 gradient buffer, h^T of one token block (H x
- * block_t bf16) plus O(T*K + T*V/256) per-token state.  It allocates no device memory, keeps no state between calls (except
- * the optional timing facility below) and is reentrant across streams given
- * distinct workspaces.
+ * the caller's workspace (see kd_topk_kl_workspace_size): two fixed
+ * block_t x chunk_v bf16 gradient buffers (one when the call has a single
+ * token block and vocabulary chunk), h^T of one token block (H x block_t
+ * bf16) plus O(T*K + T*V/256) per-token state.  It allocates no device
+ * memory, keeps no state between calls (except the optional timing
+ * facility below and the static scratch of kd_topk_kl_fwd_bwd_noalloc) and
+ * is reentrant across streams given distinct workspaces.
  */
 #ifndef KDKL_H
 #define KDKL_H
@@ -99,6 +101,14 @@ typedef struct kd_problem {
  * KD_ERR_ARG / KD_ERR_UNSUPPORTED for a problem the main call would reject. */
 kd_status kd_topk_kl_workspace_size(const kd_problem* p, size_t* bytes);
 
+/* The tiling kd_topk_kl_fwd_bwd / kd_topk_kl_bwd use for this problem (the
+ * caller's chunk_v / block_t, else the defaults): tokens per block (T
+ * rounded up to 256 when below one block), vocabulary rows per chunk, and
+ * the number of bf16 gradient buffers (2 when the call has several (block,
+ * chunk) units: unit i's contractions share a launch with unit i + 1's
+ * pass 2).  Synchronous, host only. */
+kd_status kd_topk_kl_tiling(const kd_problem* p, int64_t* block_t, int64_t* chunk_v, int32_t* gbufs);
+
 /* Forward and backward of the loss above, enqueued on `stream`.
  *
  *   h             [T,H]  bf16 bit patterns, row-major, device, 16-byte aligned
@@ -133,14 +143,16 @@ kd_status kd_topk_kl_fwd_bwd(const kd_problem* p,
  * one static device scratch array of KD_NOALLOC_SCRATCH_BYTES per GPU, from
  * its first use on that GPU until the process ends, and runs the same
  * kernels with the same tiling as kd_topk_kl_fwd_bwd (bitwise the same
- * results for the same problem).
+ * results for the same problem) through one gradient buffer instead of two
+ * (each unit's pass 2 and contractions in launches of their own).
  *
  *   Arguments as kd_topk_kl_fwd_bwd, minus workspace / workspace_bytes.  The
  *   stream must belong to the current device (KD_ERR_ARG otherwise).
- *   A problem whose workspace (kd_topk_kl_workspace_size) exceeds
- *   KD_NOALLOC_SCRATCH_BYTES returns KD_ERR_WORKSPACE before anything is
- *   enqueued; the gpt-oss-20b-like head (T 4096, H 2880, V 201088, K 64)
- *   fits with chunk_v = 8192 (114 MiB).
+ *   A problem whose single-buffer workspace (kd_topk_kl_workspace_size
+ *   less one block_t x chunk_v bf16 gradient buffer when the call has more
+ *   than one (block, chunk) unit) exceeds KD_NOALLOC_SCRATCH_BYTES returns
+ *   KD_ERR_WORKSPACE before anything is enqueued; the gpt-oss-20b-like head
+ *   (T 4096, H 2880, V 201088, K 64) fits with chunk_v = 8192 (114 MiB).
  *   The first call on a GPU looks up that GPU's scratch address
  *   (hipGetSymbolAddress); make it outside graph capture.
  *   Every call on one GPU uses the same scratch, which keeps the last call's
@@ -257,16 +269,19 @@ const char* kd_status_string(kd_status s);
 /* ABI version (incremented on any change of the declarations above; 2 adds
  * the split forward / backward entry points and the gradient flags, 3 the
  * logits variant, the top-K selection and two more timing classes, 4 the
- * timing class mask). */
+ * timing class mask, 5 the allocation-free fused call, the tiling query and
+ * timing class 11). */
 int kd_abi_version(void);
 
 /* Optional per-kernel timing with HIP events recorded on the launch stream
  * around every launch of the library's kernels while enabled.  Intended for
  * benchmarks; not thread-safe.  Kernel classes: 0 teacher, 1 gather,
- * 2 pass1, 3 lse, 4 loss, 5 pass2, 6 fixup, 7 bwd, 8 other, 9 logits (the
- * row kernel of kd_topk_kl_logits), 10 topk (kd_topk_select).
+ * 2 pass1, 3 lse, 4 loss, 5 pass2, 6 fixup (the teacher-entry buckets or
+ * the dense fixup), 7 bwd, 8 other, 9 logits (the row kernel of
+ * kd_topk_kl_logits), 10 topk (kd_topk_select), 11 bwd_pass2 (one unit's
+ * contractions with the next unit's pass 2).
  * kd_timing_collect synchronises the recorded events, adds each class's
- * elapsed milliseconds and launch count to ms[11] / launches[11] (either may
+ * elapsed milliseconds and launch count to ms[12] / launches[12] (either may
  * be NULL) and releases the events. */
 kd_status kd_timing_enable(int on);
 kd_status kd_timing_collect(double* ms, int64_t* launches);

@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol():
     L = kd.lib()
     for n in declared_functions():
         assert hasattr(L, n)
-    assert L.kd_abi_version() == kd.ABI_VERSION == 4
+    assert L.kd_abi_version() == kd.ABI_VERSION == 5
 
 
 def _ws(T, H, V, K, tau=1.0, chunk_v=0, block_t=0):
@@ -51,9 +51,10 @@ def _ws(T, H, V, K, tau=1.0, chunk_v=0, block_t=0):
 def test_workspace_plan():
     code, n = _ws(4096, 2880, 201088, 64)
     assert code == 0
-    # gradient buffer (4096 x 12288 bf16), the block's h^T (2880 x 4096 bf16)
-    # plus per-token state
-    fixed = 4096 * 12288 * 2 + 2880 * 4096 * 2
+    # two gradient buffers (4096 x 12288 bf16: one unit's contractions run
+    # beside the next unit's pass 2), the block's h^T (2880 x 4096 bf16) plus
+    # per-token state
+    fixed = 2 * 4096 * 12288 * 2 + 2880 * 4096 * 2
     assert fixed <= n < fixed + 4096 * 8 * 1024
     # per-token growth is linear once T exceeds one block
     _, a = _ws(65536, 2880, 201088, 64)
@@ -156,12 +157,12 @@ def test_split_entry_point_sizes():
     assert code == 0
     code, fwd = _size(L.kd_topk_kl_fwd_workspace_size, T, H, V, K)
     assert code == 0
-    # the forward needs no gradient buffer (4096 x 12288 bf16), no h^T (2880 x 4096 bf16),
+    # the forward needs no gradient buffers (2 x 4096 x 12288 bf16), no h^T (2880 x 4096 bf16),
     # no per-token pass-2 offsets (4096 fp32) and no bucketed teacher entries (counts and
     # cursors per (token tile, vocabulary tile), token-tile bases, one word per entry)
     r256 = lambda x: (x + 255) // 256 * 256
     nkeys = (T // 256) * ((V + 255) // 256 + 1)
-    assert full - fwd == (4096 * 12288 * 2 + H * 4096 * 2 + 4 * 4096 + r256(8 * nkeys) + r256(4 * (T // 256) + 4)
+    assert full - fwd == (2 * 4096 * 12288 * 2 + H * 4096 * 2 + 4 * 4096 + r256(8 * nkeys) + r256(4 * (T // 256) + 4)
                           + 4 * T * K)
     code, saved = _size(L.kd_topk_kl_saved_size, T, H, V, K)
     assert code == 0
@@ -175,12 +176,13 @@ def test_split_entry_point_sizes():
     assert _size(L.kd_topk_kl_workspace_size, T, H, V, K,
                  flags=kd.KD_FLAG_ACCUMULATE_DH | kd.KD_FLAG_ACCUMULATE_DW) == (0, full)
     assert _size(L.kd_topk_kl_workspace_size, T, H, V, K, flags=32)[0] == 1
-    # the sequence-chunk schedule keeps one token block of fp32 logits (block 4096 by default)
-    # and defaults to vocabulary chunks of 16384 (12288 otherwise)
+    # the sequence-chunk schedule keeps one token block of fp32 logits (block 4096 by default),
+    # one gradient buffer, and defaults to vocabulary chunks of 16384 (12288 otherwise)
     code, sq = _size(L.kd_topk_kl_workspace_size, T, H, V, K, flags=kd.KD_FLAG_SEQ_CHUNK)
-    assert code == 0 and sq - full == 4 * V * 4096 + 4096 * (16384 - 12288) * 2
+    assert code == 0 and sq - full == 4 * V * 4096 + 4096 * 16384 * 2 - 2 * 4096 * 12288 * 2
     assert _size(L.kd_topk_kl_workspace_size, T, H, V, K, flags=kd.KD_FLAG_SEQ_CHUNK, block_t=1024,
-                 chunk_v=12288)[1] - _size(L.kd_topk_kl_workspace_size, T, H, V, K, block_t=1024)[1] == 4 * V * 1024
+                 chunk_v=12288)[1] - _size(L.kd_topk_kl_workspace_size, T, H, V, K, block_t=1024)[1] == \
+        4 * V * 1024 - 1024 * 12288 * 2
     for fn in (L.kd_topk_kl_saved_size, L.kd_topk_kl_fwd_workspace_size):
         assert _size(fn, T, 2900, V, K)[0] == 2
 
@@ -249,8 +251,9 @@ def test_noalloc_rejects_problems_beyond_its_scratch_before_any_hip_call():
     assert _ws(4096, 2880, 201088, 64)[1] > kd.NOALLOC_SCRATCH_BYTES
     assert L.kd_topk_kl_fwd_bwd_noalloc(ctypes.byref(p), fake, fake, fake, fake, vp(0), fake, fake, fake,
                                         vp(0), vp(0)) == 3
-    # with 8192-row chunks it fits (checked on the GPU); argument errors come first
-    assert _ws(4096, 2880, 201088, 64, 1.0, 8192, 0)[1] <= kd.NOALLOC_SCRATCH_BYTES
+    # with 8192-row chunks its single-buffer plan (one 4096 x 8192 bf16 gradient buffer
+    # less than kd_topk_kl_workspace_size) fits (checked on the GPU); argument errors come first
+    assert _ws(4096, 2880, 201088, 64, 1.0, 8192, 0)[1] - 4096 * 8192 * 2 <= kd.NOALLOC_SCRATCH_BYTES
     assert L.kd_topk_kl_fwd_bwd_noalloc(ctypes.byref(p), fake, vp(0), fake, fake, vp(0), fake, fake, fake,
                                         vp(0), vp(0)) == 1
     bad = kd.problem(16, 64, 100, 4, tau=0.0)
