@@ -47,6 +47,7 @@ struct Plan {
   int gt1, gt2;      // token-tile group sizes of pass 1 / pass 2
   int gv1, gv2;      // vocabulary group sizes (take precedence when > 0)
   int gm_dh, gm_dw;  // hidden-tile group sizes of the gradient contractions
+  int bm;            // hidden rows of a gradient-contraction tile
   int64_t ldp;       // leading dim of the pass-1 partials
   int64_t grows;     // rows of the gradient buffer
   int64_t nunits;    // (token block, vocabulary chunk) units of the gradient pass
@@ -58,11 +59,12 @@ struct Plan {
   size_t o_S;        // seq: S^T of one block, [V, Tb] fp32
   size_t o_hT;       // h^T of one token block, [H, Tb] bf16 (gradient pass)
   size_t o_off;      // per-token pass-2 offsets [Tp] (gradient pass)
-  // teacher entries by (token tile, vocabulary tile) (gradient pass):
-  // counts / starts [ntt_all, ldk] then fill cursors [ntt_all, ldk]
-  // (contiguous, cleared together), token-tile bases, entries [T*K]
+  // teacher entries by (token tile, vocabulary tile): counts / starts
+  // [ntt_all, ldk] then fill cursors [ntt_all, ldk] (contiguous, cleared
+  // together), token-tile bases [ntt_all + 1], entries and their flat
+  // indices [T*K]
   int ntt_all, ldk;
-  size_t o_bcnt, o_bcur, o_bbase, o_ent;
+  size_t o_bcnt, o_bcur, o_bbase, o_ent, o_enti;
   size_t o_G, o_dhs, o_dws, o_part, o_lse2, o_p, o_pm, o_s, o_neg, o_row, o_bsum, o_scal_f, o_scal_i, o_status, total;
 };
 
@@ -129,6 +131,10 @@ Plan make_plan(const kd_problem* p, bool with_grad = true, bool one_gbuf = false
   P.gv2 = env_int("KDKL_GROUP_V2", 8);
   P.gm_dh = std::max(1, env_int("KDKL_GROUP_MDH", 6));
   P.gm_dw = std::max(1, env_int("KDKL_GROUP_MDW", 4));
+  // 256-row contraction tiles: at H = 2880 the last one holds 64 rows, but
+  // 192-row tiles (2880 = 15 x 192, bitwise the same results) measured
+  // slower (one fourth more fragment reads and loads per flop)
+  P.bm = 256;
   if (P.gt1 < 1) P.gt1 = 1;
   if (P.gt2 < 1) P.gt2 = 1;
   P.ldp = (int64_t)P.ntt_max * 256;
@@ -147,10 +153,11 @@ Plan make_plan(const kd_problem* p, bool with_grad = true, bool one_gbuf = false
   P.ntt_all = (int)cdiv(P.T, 256);
   P.ldk = (int)P.nvt + 1;
   const size_t nkeys = (size_t)P.ntt_all * P.ldk;
-  P.o_bcnt = with_grad ? take(nkeys * 8) : 0;  // counts then cursors: one region
+  P.o_bcnt = take(nkeys * 8);  // counts then cursors: one region
   P.o_bcur = P.o_bcnt + nkeys * 4;
-  P.o_bbase = with_grad ? take((size_t)P.ntt_all * 4 + 4) : 0;
-  P.o_ent = with_grad ? take((size_t)P.T * P.K * 4) : 0;
+  P.o_bbase = take((size_t)P.ntt_all * 4 + 4);
+  P.o_ent = take((size_t)P.T * P.K * 4);
+  P.o_enti = take((size_t)P.T * P.K * 4);
   P.o_S = P.seq ? take((size_t)P.V * P.Tb * 4) : 0;
   const bool stage = with_grad && (p->flags & KD_FLAG_GRAD_BF16);
   // both schedules walk token blocks in the outer loop: a block's dH is
@@ -235,7 +242,7 @@ struct Bufs {
   uint16_t* G;
   uint16_t* hT;  // h^T of one token block (gradient pass)
   float* off;    // pass-2 offsets (gradient pass)
-  uint32_t *bcnt, *bcur, *bbase, *ent;  // teacher entries by tile (gradient pass)
+  uint32_t *bcnt, *bcur, *bbase, *ent, *enti;  // teacher entries by tile
   float* dhs;   // fp32 staging of a bf16 dH (nullable)
   float* dws;   // fp32 staging of one chunk of a bf16 dW (nullable)
   float2* part;
@@ -257,10 +264,11 @@ Bufs carve(const Plan& P, void* workspace, bool with_grad) {
   b.G = with_grad ? reinterpret_cast<uint16_t*>(ws + P.o_G) : nullptr;
   b.hT = with_grad ? reinterpret_cast<uint16_t*>(ws + P.o_hT) : nullptr;
   b.off = with_grad ? reinterpret_cast<float*>(ws + P.o_off) : nullptr;
-  b.bcnt = with_grad ? reinterpret_cast<uint32_t*>(ws + P.o_bcnt) : nullptr;
-  b.bcur = with_grad ? reinterpret_cast<uint32_t*>(ws + P.o_bcur) : nullptr;
-  b.bbase = with_grad ? reinterpret_cast<uint32_t*>(ws + P.o_bbase) : nullptr;
-  b.ent = with_grad ? reinterpret_cast<uint32_t*>(ws + P.o_ent) : nullptr;
+  b.bcnt = reinterpret_cast<uint32_t*>(ws + P.o_bcnt);
+  b.bcur = reinterpret_cast<uint32_t*>(ws + P.o_bcur);
+  b.bbase = reinterpret_cast<uint32_t*>(ws + P.o_bbase);
+  b.ent = reinterpret_cast<uint32_t*>(ws + P.o_ent);
+  b.enti = reinterpret_cast<uint32_t*>(ws + P.o_enti);
   b.dhs = with_grad && P.o_dhs ? reinterpret_cast<float*>(ws + P.o_dhs) : nullptr;
   b.dws = with_grad && P.o_dws ? reinterpret_cast<float*>(ws + P.o_dws) : nullptr;
   b.part = reinterpret_cast<float2*>(ws + P.o_part);
@@ -308,38 +316,51 @@ void launch_prep(Launcher& L, const Plan& P, const Inputs& in, const Bufs& b, bo
   });
 }
 
-// s[t,k] = <h_t, W_idx[t,k]>: the register-row variant for H <= 8192.
-void launch_gather(Launcher& L, const Inputs& in, int64_t T, int64_t H, int64_t V, int K, float* s_out) {
-  using namespace kd;
+// Teacher entries of kept tokens bucketed by (token tile, vocabulary tile):
+// counts, the two scans, placement with their cached slots.
+void launch_bucket_index(Launcher& L, const Plan& P, const Inputs& in, const Bufs& b) {
   hipStream_t s = L.s;
-  const unsigned g = (unsigned)T;
-  const int64_t nj = cdiv(H, 512);
-  L.run(1, [&] {
-    if (nj <= 2)
-      k_gather_r<2><<<g, 256, 0, s>>>(in.h, in.W, in.idx, in.mask, T, H, V, K, s_out);
-    else if (nj <= 4)
-      k_gather_r<4><<<g, 256, 0, s>>>(in.h, in.W, in.idx, in.mask, T, H, V, K, s_out);
-    else if (nj <= 6)
-      k_gather_r<6><<<g, 256, 0, s>>>(in.h, in.W, in.idx, in.mask, T, H, V, K, s_out);
-    else if (nj <= 8)
-      k_gather_r<8><<<g, 256, 0, s>>>(in.h, in.W, in.idx, in.mask, T, H, V, K, s_out);
-    else if (nj <= 12)
-      k_gather_r<12><<<g, 256, 0, s>>>(in.h, in.W, in.idx, in.mask, T, H, V, K, s_out);
-    else if (nj <= 16)
-      k_gather_r<16><<<g, 256, 0, s>>>(in.h, in.W, in.idx, in.mask, T, H, V, K, s_out);
-    else
-      k_gather<<<g, 256, 0, s>>>(in.h, in.W, in.idx, in.mask, T, H, V, K, s_out);
+  using namespace kd;
+  const int64_t T = P.T, n = T * P.K;
+  const int64_t nkeys = (int64_t)P.ntt_all * P.ldk;
+  L.run(6, [&] {
+    k_fill<<<grid_fill(2 * nkeys, 256), 256, 0, s>>>(reinterpret_cast<float*>(b.bcnt), 2 * nkeys, 0.f);
+  });
+  L.run(6, [&] {
+    k_bucket_count<<<(unsigned)cdiv(n, 256), 256, 0, s>>>(in.idx, in.mask, T, P.K, P.V, P.ldk, b.bcnt);
+  });
+  L.run(6, [&] { k_scan_rows<<<(unsigned)P.ntt_all, 1024, 0, s>>>(b.bcnt, (int)P.nvt, P.ldk); });
+  L.run(6, [&] { k_scan_tiles<<<1, 1024, 0, s>>>(b.bcnt, P.ntt_all, P.ldk, (int)P.nvt, b.bbase); });
+  L.run(6, [&] {
+    k_bucket_index<<<(unsigned)cdiv(n, 256), 256, 0, s>>>(in.idx, in.mask, T, P.K, P.V, P.ldk, b.bcnt, b.bbase,
+                                                          b.bcur, b.ent, b.enti);
   });
 }
 
-// Gather, pass 1 (per-token log-sum-exp), per-row loss and the mean.
+// The placed entries' logit-gradient values (after pass 1 and the gather).
+void launch_bucket_value(Launcher& L, const Plan& P, const Bufs& b) {
+  hipStream_t s = L.s;
+  using namespace kd;
+  const int64_t n = P.T * P.K;
+  L.run(6, [&] {
+    k_bucket_value<<<(unsigned)cdiv(n, 256), 256, 0, s>>>(b.s, b.pm, b.lse2, b.scal_f, P.K, kLog2e / P.tau,
+                                                          b.bbase + P.ntt_all, b.enti, b.ent);
+  });
+}
+
+// Teacher entries bucketed by tile, pass 1 (per-token log-sum-exp, and the
+// logits at the cached ids), per-row loss and the mean.
 void launch_forward(Launcher& L, const Plan& P, const Inputs& in, const Bufs& b, float* loss, float* row_loss) {
   hipStream_t s = L.s;
   using namespace kd;
   const int64_t T = P.T, H = P.H, V = P.V;
   const int K = P.K;
   const float c = kLog2e / P.tau;
-  launch_gather(L, in, T, H, V, K, b.s);
+  // the student logits at the cached ids come out of pass 1's own tiles,
+  // through the entries bucketed by tile (slots of masked tokens and
+  // out-of-range ids read 0)
+  L.run(1, [&] { k_fill<<<grid_fill(T * K, 256), 256, 0, s>>>(b.s, T * K, 0.f); });
+  launch_bucket_index(L, P, in, b);
   for (int64_t t0 = 0; t0 < T; t0 += P.Tb) {
     const int64_t rows = std::min<int64_t>(P.Tb, T - t0);
     Pass1Args a{};
@@ -356,6 +377,13 @@ void launch_forward(Launcher& L, const Plan& P, const Inputs& in, const Bufs& b,
     a.total = a.ntt * a.nvt;
     a.ldp = (int)P.ldp;
     a.c = c;
+    a.bstart = b.bcnt;
+    a.bbase = b.bbase;
+    a.ent = b.ent;
+    a.s_out = b.s;
+    a.ldk = P.ldk;
+    a.gtt0 = (int)(t0 / 256);
+    a.K = K;
     const int grid = (int)(cdiv(a.total, 8) * 8);
     L.run(2, [&] { k_pass1<false><<<grid, 256, 0, s>>>(a); });
     L.run(3, [&] {
@@ -378,26 +406,10 @@ void launch_transpose_h(Launcher& L, const Plan& P, const Inputs& in, const Bufs
   L.run(8, [&] { kd::k_transpose_h<<<grid, 256, 0, s>>>(in.h + t0 * P.H, rows, P.H, b.hT, P.Tb); });
 }
 
-// Teacher entries of kept tokens bucketed by (token tile, vocabulary tile),
-// each with its final logit-gradient value: counts, the two scans, fill.
-void launch_buckets(Launcher& L, const Plan& P, const Inputs& in, const Bufs& b) {
+// The gradient contractions of one unit alone (k_bwd at the plan's tile height).
+void launch_bwd(Launcher& L, const Plan& P, const kd::BwdArgs& g, int grid) {
   hipStream_t s = L.s;
-  using namespace kd;
-  const int64_t T = P.T, n = T * P.K;
-  const int64_t nkeys = (int64_t)P.ntt_all * P.ldk;
-  const float c = kLog2e / P.tau;
-  L.run(6, [&] {
-    k_fill<<<grid_fill(2 * nkeys, 256), 256, 0, s>>>(reinterpret_cast<float*>(b.bcnt), 2 * nkeys, 0.f);
-  });
-  L.run(6, [&] {
-    k_bucket_count<<<(unsigned)cdiv(n, 256), 256, 0, s>>>(in.idx, in.mask, T, P.K, P.V, P.ldk, b.bcnt);
-  });
-  L.run(6, [&] { k_scan_rows<<<(unsigned)P.ntt_all, 1024, 0, s>>>(b.bcnt, (int)P.nvt, P.ldk); });
-  L.run(6, [&] { k_scan_tiles<<<1, 1024, 0, s>>>(b.bcnt, P.ntt_all, P.ldk, (int)P.nvt, b.bbase); });
-  L.run(6, [&] {
-    k_bucket_fill<<<(unsigned)cdiv(n, 256), 256, 0, s>>>(in.idx, b.s, b.pm, b.lse2, in.mask, b.scal_f, T, P.K, P.V,
-                                                         c, P.ldk, b.bcnt, b.bbase, b.bcur, b.ent);
-  });
+  L.run(7, [&] { kd::k_bwd<4><<<grid, 256, 0, s>>>(g); });
 }
 
 // Pass 2: for each token block (outer) and vocabulary chunk (inner),
@@ -408,7 +420,7 @@ void launch_buckets(Launcher& L, const Plan& P, const Inputs& in, const Bufs& b)
 // once; its dH rows are final after its last chunk, a dW chunk after the
 // last block.
 void launch_backward(Launcher& L, const Plan& P, uint32_t flags, const Inputs& in, const Bufs& b, void* dH_out,
-                     void* dW_out) {
+                     void* dW_out, bool have_index) {
   hipStream_t s = L.s;
   using namespace kd;
   const int64_t T = P.T, H = P.H, V = P.V;
@@ -417,13 +429,14 @@ void launch_backward(Launcher& L, const Plan& P, uint32_t flags, const Inputs& i
   const bool acc_dh_in = (flags & KD_FLAG_ACCUMULATE_DH) != 0;
   const bool acc_dw_in = (flags & KD_FLAG_ACCUMULATE_DW) != 0;
   const bool whole_dw = T > P.Tb;  // bf16 dW staging holds all of dW
-  const int nht = (int)cdiv(H, 256);
+  const int nht = (int)cdiv(H, P.bm);
   const int64_t Tp = align256(T);
   const size_t gbuf = (size_t)P.grows * P.chunk_v;  // elements of one gradient buffer
   L.run(8, [&] {
     k_offsets<<<(unsigned)cdiv(Tp, 256), 256, 0, s>>>(b.lse2, in.mask, T, Tp, b.scal_f, b.off);
   });
-  launch_buckets(L, P, in, b);
+  if (!have_index) launch_bucket_index(L, P, in, b);
+  launch_bucket_value(L, P, b);
   struct Unit {
     int64_t t0, rows, v0, vrows;
     int bi, ci;
@@ -510,13 +523,13 @@ void launch_backward(Launcher& L, const Plan& P, uint32_t flags, const Inputs& i
     const int nb = u.g.ndh_pad + u.g.ndw_pad;
     if (!merged) {
       L.run(5, [&] { k_pass2<<<pad8(u.p.total), 256, 0, s>>>(u.p); });
-      L.run(7, [&] { k_bwd<<<nb, 256, 0, s>>>(u.g); });
+      launch_bwd(L, P, u.g, nb);
     } else if (i + 1 < units.size()) {
       const Pass2Args& pn = units[i + 1].p;
       const int p_pad = pad8(pn.total);
-      L.run(11, [&] { k_bwd_pass2<<<nb + p_pad, 256, 0, s>>>(u.g, pn, p_pad); });
+      L.run(11, [&] { k_bwd_pass2<4><<<nb + p_pad, 256, 0, s>>>(u.g, pn, p_pad); });
     } else {
-      L.run(7, [&] { k_bwd<<<nb, 256, 0, s>>>(u.g); });
+      launch_bwd(L, P, u.g, nb);
     }
     if (dW_out && bf16 && !whole_dw) {
       const int64_t n = u.vrows * H;
@@ -553,7 +566,7 @@ void launch_seq(Launcher& L, const Plan& P, uint32_t flags, const Inputs& in, co
   const bool acc_dw_in = (flags & KD_FLAG_ACCUMULATE_DW) != 0;
   float* dH = dH_out ? (bf16 ? b.dhs : static_cast<float*>(dH_out)) : nullptr;
   const bool whole_dw = T > P.Tb;  // bf16 staging holds all of dW
-  const int nht = (int)cdiv(H, 256);
+  const int nht = (int)cdiv(H, P.bm);
   const int64_t lds = P.Tb;
   int bi = 0;
   for (int64_t t0 = 0; t0 < T; t0 += P.Tb, ++bi) {
@@ -634,7 +647,7 @@ void launch_seq(Launcher& L, const Plan& P, uint32_t flags, const Inputs& in, co
       g.grows = (int)P.grows;
       g.acc_dh = ci > 0 || (acc_dh_in && !bf16);
       g.acc_dw = bi > 0 || (acc_dw_in && !bf16);
-      L.run(7, [&] { k_bwd<<<g.ndh_pad + g.ndw_pad, 256, 0, s>>>(g); });
+      launch_bwd(L, P, g, g.ndh_pad + g.ndw_pad);
       if (dW_out && bf16 && !whole_dw) {
         const int64_t n = vrows * H;
         uint16_t* dst = static_cast<uint16_t*>(dW_out) + v0 * H;
@@ -719,7 +732,7 @@ kd_status fwd_bwd_run(const kd_problem* p, const uint16_t* h, const uint16_t* W,
     return finish(L, validate, b.status);
   }
   launch_forward(L, P, in, b, loss, row_loss);
-  if (dH || dW) launch_backward(L, P, p->flags, in, b, dH, dW);
+  if (dH || dW) launch_backward(L, P, p->flags, in, b, dH, dW, true);
   return finish(L, validate, b.status);
 }
 
@@ -919,7 +932,7 @@ kd_status kd_topk_kl_bwd(const kd_problem* p, const uint16_t* h, const uint16_t*
   }
   if (!dH && !dW) return KD_OK;
   launch_prep(L, P, in, b, validate, grad_loss);
-  launch_backward(L, P, p->flags, in, b, dH, dW);
+  launch_backward(L, P, p->flags, in, b, dH, dW, false);
   return finish(L, validate, b.status);
 }
 

@@ -11,16 +11,20 @@
 //   pass 1 : k_pass1   S^T tile = W_tile h_tile^T (MFMA), per token the
 //                      tile's (max, sum 2^(c S - max))
 //            k_lse     merges the per-tile partials -> lse2[t] (log2 units)
+//            (and, through the teacher entries bucketed by tile, the logit
+//            s[t,k] = S[t, idx[t,k]] at each cached id, read out of the tile)
 //   teacher: k_teacher p = softmax_K(u/tau), merged mass of duplicate ids,
-//                      sum_k p log(mass) per row; k_gather(_r) s[t,k] = S[t, idx]
+//                      sum_k p log(mass) per row
 //   loss   : k_rows / k_sum   KL_t = sum p log p - sum p s / tau + LSE_t
 //   pass 2 : k_pass2   recomputes the S^T tile, writes the logit gradient
 //                      G = coef * 2^(c S - lse2) (bf16) for one (token block,
 //                      vocabulary chunk), with the per-token offsets of
-//                      k_offsets; k_fixup subtracts the teacher mass at the
-//                      cached ids; k_bwd contracts G into dH (over the chunk's
-//                      vocabulary) and dW (over the block's tokens, with h^T
-//                      from k_transpose_h).
+//                      k_offsets, the bucketed teacher entries written in
+//                      place (coef * (q - mass) at the cached ids); k_bwd
+//                      contracts G into dH (over the chunk's vocabulary) and
+//                      dW (over the block's tokens, with h^T from
+//                      k_transpose_h); k_bwd_pass2 runs one unit's
+//                      contractions with the next unit's pass 2.
 #pragma once
 #include "kd_gemm.hpp"
 
@@ -148,88 +152,6 @@ __global__ void __launch_bounds__(256) k_teacher(const int32_t* __restrict__ idx
   if (lane == 0) negent[t] = ne;
 }
 
-// s[t,k] = <h[t,:], W[idx[t,k],:]> in fp32 (the student logit at each cached
-// teacher id).  One block per token, one wave per cached entry at a time.
-__global__ void __launch_bounds__(256) k_gather(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W,
-                                                const int32_t* __restrict__ idx, const uint8_t* __restrict__ mask,
-                                                int64_t T, int64_t H, int64_t V, int K, float* __restrict__ s_out) {
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int64_t t = blockIdx.x;
-  if (t >= T) return;
-  const bool keep = mask ? mask[t] != 0 : true;
-  const __amdgpu_buffer_rsrc_t rh = make_rsrc(h + t * H, (uint64_t)H * 2);
-  const int nvec = (int)(H >> 3);
-  for (int k = w; k < K; k += 4) {
-    const int32_t v = __builtin_amdgcn_readfirstlane(idx[t * K + k]);
-    float acc = 0.f;
-    if (keep && v >= 0 && (int64_t)v < V) {
-      const __amdgpu_buffer_rsrc_t rw = make_rsrc(W + (int64_t)v * H, (uint64_t)H * 2);
-      for (int j = lane; j < nvec; j += 64) {
-        const u32x4 a = buf_load16(rh, (uint32_t)j * 16u);
-        const u32x4 b = buf_load16(rw, (uint32_t)j * 16u);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          acc = fmaf(bf16_to_f32(a[q] & 0xFFFFu), bf16_to_f32(b[q] & 0xFFFFu), acc);
-          acc = fmaf(bf16_to_f32(a[q] >> 16), bf16_to_f32(b[q] >> 16), acc);
-        }
-      }
-    }
-    acc = wave_sum(acc);
-    if (lane == 0) s_out[t * K + k] = acc;
-  }
-}
-
-// The same with the token's h row held in registers (H <= 512 * NJ) and two
-// cached entries per wave at a time, their W rows read with nontemporal
-// loads (a row is read once per entry that names it).
-template <int NJ>
-__global__ void __launch_bounds__(256) k_gather_r(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W,
-                                                  const int32_t* __restrict__ idx, const uint8_t* __restrict__ mask,
-                                                  int64_t T, int64_t H, int64_t V, int K, float* __restrict__ s_out) {
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int64_t t = blockIdx.x;
-  if (t >= T) return;
-  const bool keep = mask ? mask[t] != 0 : true;
-  const __amdgpu_buffer_rsrc_t rh = make_rsrc(h + t * H, (uint64_t)H * 2);
-  u32x4 hv[NJ];  // vector lane + 64 jj of the row; zeros past H
-#pragma unroll
-  for (int jj = 0; jj < NJ; ++jj) hv[jj] = buf_load16(rh, (uint32_t)(lane + 64 * jj) * 16u);
-  for (int k = w; k < K; k += 8) {
-    const int k2 = k + 4;
-    const int32_t v0 = __builtin_amdgcn_readfirstlane(idx[t * K + k]);
-    const int32_t v1 = k2 < K ? __builtin_amdgcn_readfirstlane(idx[t * K + k2]) : -1;
-    const bool ok0 = keep && v0 >= 0 && (int64_t)v0 < V;
-    const bool ok1 = keep && v1 >= 0 && (int64_t)v1 < V;
-    // an entry that is dropped reads nothing (empty range) and sums to 0
-    const __amdgpu_buffer_rsrc_t r0 = make_rsrc(ok0 ? W + (int64_t)v0 * H : W, ok0 ? (uint64_t)H * 2 : 0);
-    const __amdgpu_buffer_rsrc_t r1 = make_rsrc(ok1 ? W + (int64_t)v1 * H : W, ok1 ? (uint64_t)H * 2 : 0);
-    u32x4 b0[NJ], b1[NJ];
-#pragma unroll
-    for (int jj = 0; jj < NJ; ++jj) {
-      const int o = (lane + 64 * jj) * 16;
-      b0[jj] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r0, o, 0, 2));
-      b1[jj] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r1, o, 0, 2));
-    }
-    float acc0 = 0.f, acc1 = 0.f;
-#pragma unroll
-    for (int jj = 0; jj < NJ; ++jj)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float hl = bf16_to_f32(hv[jj][q] & 0xFFFFu), hh = bf16_to_f32(hv[jj][q] >> 16);
-        acc0 = fmaf(hl, bf16_to_f32(b0[jj][q] & 0xFFFFu), acc0);
-        acc0 = fmaf(hh, bf16_to_f32(b0[jj][q] >> 16), acc0);
-        acc1 = fmaf(hl, bf16_to_f32(b1[jj][q] & 0xFFFFu), acc1);
-        acc1 = fmaf(hh, bf16_to_f32(b1[jj][q] >> 16), acc1);
-      }
-    acc0 = wave_sum(acc0);
-    acc1 = wave_sum(acc1);
-    if (lane == 0) {
-      s_out[t * K + k] = acc0;
-      if (k2 < K) s_out[t * K + k2] = acc1;
-    }
-  }
-}
-
 // ----------------------------------------------------------------- pass 1
 // Grid: padded to a multiple of 8; work id -> (token tile, vocabulary tile),
 // both of 256.  Each workgroup writes one (max, sum) pair per token of its
@@ -244,6 +166,13 @@ struct Pass1Args {
   float c;               // log2(e) / tau
   float* St;             // kStore: S^T of the block, [V rows, lds] fp32 (row v, column t)
   int64_t lds;
+  // !kStore: the teacher entries by tile (nullable: no gather), and where
+  // the gathered logits go (s_out[t * K + k], t global)
+  const uint32_t* bstart;
+  const uint32_t* bbase;
+  const uint32_t* ent;
+  float* s_out;
+  int ldk, gtt0, K;
 };
 
 // Writes the raw logits S^T[v, t] of the tile's valid vocabulary rows (the
@@ -290,6 +219,50 @@ __device__ __forceinline__ void store_tile_t(const Pass1Args& a, const Stages& s
   }
 }
 
+// The student logits at the cached teacher ids of this tile (its bucket of
+// entries [e0, e1), entry = t | v << 8 | k << 16 within the tile): the
+// tile's fp32 S^T passes through the four free LDS stages in two halves of
+// 128 vocabulary rows, laid out as in store_tile_t, and each entry of a
+// half reads its logit there and stores it at (t, k).  ent0 is the
+// workgroup's first entries, loaded earlier (one per thread).
+__device__ __forceinline__ void gather_tile_t(const Pass1Args& a, Stages st, const f32x16 (&acc)[4][4],
+                                              int tt, int wm, int wn, int lane, uint32_t e0, uint32_t e1,
+                                              uint32_t ent0) {
+  auto row = [&](int r) -> float* {
+    uint16_t* b = r < 32 ? st.a0 : r < 64 ? st.a1 : r < 96 ? st.b0 : st.b1;
+    return reinterpret_cast<float*>(b) + (r & 31) * 256;
+  };
+  const int tid = threadIdx.x;
+  const int64_t t0 = ((int64_t)a.gtt0 + tt) * 256;
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    if (wm == half) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int r = acc_row(i, e, lane);
+          float* rp = row(r);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int t = wn * 128 + acc_col(j, lane);
+            rp[(((t >> 2) ^ (8 * ((r >> 2) & 1))) << 2) | (t & 3)] = acc[i][j][e];
+          }
+        }
+    }
+    __syncthreads();
+    auto take = [&](uint32_t x) {
+      const int tl = x & 255, vr = (x >> 8) & 255, k = (int)(x >> 16);
+      if ((vr >> 7) != half) return;
+      const int r = vr & 127;
+      a.s_out[(t0 + tl) * a.K + k] = row(r)[(((tl >> 2) ^ (8 * ((r >> 2) & 1))) << 2) | (tl & 3)];
+    };
+    if (e0 + (uint32_t)tid < e1) take(ent0);
+    for (uint32_t e = e0 + 256 + tid; e < e1; e += 256) take(a.ent[e]);
+    __syncthreads();
+  }
+}
+
 // One (token tile, vocabulary tile) per workgroup: S^T of the tile, then per
 // token the tile's max m and sum l of 2^(c S - m) (base-2 log-sum-exp parts),
 // folded across tiles by k_lse.  Nothing but the loaders lives across the K
@@ -307,6 +280,15 @@ __global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 
     grouped(id, a.ntt, a.nvt, a.gt, tt, vt);
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int wm = w & 1, wn = w >> 1;
+  // this tile's teacher entries: [e0, e1) of a.ent
+  uint32_t e0 = 0, e1 = 0;
+  if (!kStore && a.ent) {
+    const int gtt = a.gtt0 + tt;
+    const int64_t key = (int64_t)gtt * a.ldk + vt;
+    const uint32_t bb = a.bbase[gtt];
+    e0 = bb + a.bstart[key];
+    e1 = bb + a.bstart[key + 1];
+  }
   f32x16 acc[4][4];
   {
     LoaderKC<256> la, lb;
@@ -314,6 +296,8 @@ __global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 
     lb.init(a.h + (int64_t)tt * 256 * a.H, a.rows - (int64_t)tt * 256, a.H);
     gemm_tile<4, 4>(la, lb, (int)(a.H / kBK), st, acc);
   }
+  // first entries now: their latency hides under the exponentials below
+  const uint32_t ent0 = e0 + threadIdx.x < e1 ? a.ent[e0 + threadIdx.x] : 0u;
   // vocabulary rows of this lane: vt*256 + wm*128 + acc_row(i, e)
   const int64_t vbase = (int64_t)vt * 256 + wm * 128;
   if constexpr (kStore) store_tile_t(a, st, acc, vt, tt, wm, wn, lane);
@@ -380,6 +364,9 @@ __global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 
       const int t = tt * 256 + wn * 128 + acc_col(j, lane);
       a.part[(int64_t)vt * a.ldp + t] = make_float2(rm[j], rl[j]);
     }
+  }
+  if constexpr (!kStore) {
+    if (e1 > e0) gather_tile_t(a, st, acc, tt, wm, wn, lane, e0, e1, ent0);
   }
 }
 
@@ -461,13 +448,16 @@ __global__ void __launch_bounds__(1024) k_sum(const double* __restrict__ bsum, i
 // --------------------------------------------- teacher entries by tile
 // The cached teacher entries of kept tokens, grouped by the (token tile,
 // vocabulary tile) of 256 x 256 they fall in (the per-chunk bucketing of
-// the teacher ids), each carrying its final logit-gradient value
-// bf16(coef * (q - mass)) with q = 2^(c s - lse2) from the gathered student
-// logit: the pass-2 workgroup of that tile writes them into its staged tile.
+// the teacher ids).  The pass-1 workgroup of a tile reads the student logit
+// at each of its entries out of its own logit tile; then every entry gets
+// its final logit-gradient value bf16(coef * (q - mass)), q = 2^(c s - lse2),
+// which the pass-2 workgroup of that tile writes into its staged tile.
 // Bucket (tt, vt) is slot tt * ldk + vt, ldk = nvt + 1; after the scans slot
 // (tt, vt) holds the bucket's start relative to the token tile's first
 // entry, slot (tt, nvt) the token tile's count, and base[tt] the token
-// tile's first entry.  An entry is (t & 255) | (v & 255) << 8 | bits << 16.
+// tile's first entry.  Before pass 1 an entry is (t & 255) | (v & 255) << 8
+// | k << 16 (token and id within the tile, cached slot); after,
+// (t & 255) | (v & 255) << 8 | bits << 16.
 __global__ void k_bucket_count(const int32_t* __restrict__ idx, const uint8_t* __restrict__ mask, int64_t T, int K,
                                int64_t V, int ldk, uint32_t* __restrict__ cnt) {
   const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
@@ -508,7 +498,8 @@ __global__ void __launch_bounds__(1024) k_scan_rows(uint32_t* __restrict__ data,
 }
 
 // base[tt] = first entry of token tile tt (exclusive scan of the tile
-// totals that k_scan_rows left in slot nvt of each row); one workgroup.
+// totals that k_scan_rows left in slot nvt of each row), base[ntt] = the
+// number of entries; one workgroup.
 __global__ void __launch_bounds__(1024) k_scan_tiles(const uint32_t* __restrict__ start, int ntt, int ldk, int nvt,
                                                       uint32_t* __restrict__ base) {
   __shared__ uint32_t part[1024];
@@ -530,18 +521,17 @@ __global__ void __launch_bounds__(1024) k_scan_tiles(const uint32_t* __restrict_
     base[i] = run;
     run += start[(int64_t)i * ldk + nvt];
   }
+  if (j == 1023) base[ntt] = part[1023];
 }
 
-// Places every kept entry in its bucket (order inside a bucket is free: two
-// entries of one (t, v), duplicate ids, carry the same value) with its
-// gradient value, the same arithmetic as the dense fixup of the
-// sequence-chunk schedule (k_fixup).
-__global__ void k_bucket_fill(const int32_t* __restrict__ idx, const float* __restrict__ s,
-                              const float* __restrict__ pm, const float* __restrict__ lse2,
-                              const uint8_t* __restrict__ mask, const float* __restrict__ scal_f, int64_t T, int K,
-                              int64_t V, float c, int ldk, const uint32_t* __restrict__ start,
-                              const uint32_t* __restrict__ base, uint32_t* __restrict__ cur,
-                              uint32_t* __restrict__ ent) {
+// Places every kept entry in its bucket (order inside a bucket is free) as
+// t | v << 8 | k << 16 (token and id within their tiles, cached slot), and
+// its flat index t * K + k beside it: pass 1 gathers the logits through
+// these, then k_bucket_value turns them into the pass-2 entries.
+__global__ void k_bucket_index(const int32_t* __restrict__ idx, const uint8_t* __restrict__ mask, int64_t T, int K,
+                               int64_t V, int ldk, const uint32_t* __restrict__ start,
+                               const uint32_t* __restrict__ base, uint32_t* __restrict__ cur,
+                               uint32_t* __restrict__ ent, uint32_t* __restrict__ ent_i) {
   const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
   if (i >= T * K) return;
   const int64_t t = i / K;
@@ -550,10 +540,27 @@ __global__ void k_bucket_fill(const int32_t* __restrict__ idx, const float* __re
   if (v < 0 || (int64_t)v >= V) return;
   const int64_t key = (t >> 8) * ldk + (v >> 8);
   const uint32_t pos = base[t >> 8] + start[key] + atomicAdd(cur + key, 1u);
+  ent[pos] = (uint32_t)(t & 255) | ((uint32_t)(v & 255) << 8) | ((uint32_t)(i - t * K) << 16);
+  ent_i[pos] = (uint32_t)i;
+}
+
+// Each placed entry (position p < base[ntt], the number placed) gets its
+// final logit-gradient value bf16(coef * (q - mass)), q = 2^(c s - lse2)
+// from the gathered logit, in place of its slot: t | v << 8 | bits << 16.
+// The same arithmetic as the dense fixup of the sequence-chunk schedule
+// (k_fixup).
+__global__ void k_bucket_value(const float* __restrict__ s, const float* __restrict__ pm,
+                               const float* __restrict__ lse2, const float* __restrict__ scal_f, int K, float c,
+                               const uint32_t* __restrict__ total, const uint32_t* __restrict__ ent_i,
+                               uint32_t* __restrict__ ent) {
+  const int64_t p = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (p >= (int64_t)total[0]) return;
+  const uint32_t i = ent_i[p];
+  const uint32_t t = i / (uint32_t)K;
   const float q = fast_exp2(fmaf(s[i], c, -lse2[t]));
   const float g = scal_f[0] * (q - pm[i]);
   const uint32_t bits = __builtin_bit_cast(uint16_t, (__bf16)g);
-  ent[pos] = (uint32_t)(t & 255) | ((uint32_t)(v & 255) << 8) | (bits << 16);
+  ent[p] = (ent[p] & 0xFFFFu) | (bits << 16);
 }
 
 // ----------------------------------------------------------------- pass 2
@@ -841,15 +848,17 @@ struct BwdArgs {
   int acc_dh, acc_dw;     // accumulate (1) or overwrite (0)
 };
 
-// Grid: [0, ndh_pad) dH work, then [ndh_pad, ndh_pad + ndw_pad) dW work;
-// inside each segment the 8 XCDs get contiguous work ranges (idle padding
-// workgroups exit at once).  dH tiles come first: their K loop (the chunk's
-// vocabulary) is the longer one.
-// One gradient-contraction workgroup, linear id L of the k_bwd grid.
+// One gradient-contraction workgroup, linear id L of the k_bwd grid.  The
+// output tile is (64 MI) hidden units x 256: MI = 4 (256 rows), or MI = 3
+// (192 rows, for hidden sizes that 192 divides and 256 does not, e.g.
+// 2880 = 15 x 192, where 256-row tiles would leave a quarter-full last
+// tile of zero rows in every contraction).
+template <int MI>
 __device__ __forceinline__ void bwd_tile(const BwdArgs& a, int L, Stages st) {
+  constexpr int BM = 64 * MI;  // hidden rows of the tile
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int wm = w & 1, wn = w >> 1;
-  f32x16 acc[4][4];
+  f32x16 acc[MI][4];
   float* out;
   int64_t nvalid;
   int mt, nt, acc_mode;
@@ -857,11 +866,11 @@ __device__ __forceinline__ void bwd_tile(const BwdArgs& a, int L, Stages st) {
     const int id = xcd_remap(L, a.ndh_pad);
     if (id >= a.ndh) return;
     grouped(id, a.nht, a.ntt, a.gm_dh, mt, nt);
-    LoaderTR la;
+    LoaderTR<BM> la;
     LoaderKC<256> lb;
-    la.init(a.W, a.vrows, a.H, mt * 256);
+    la.init(a.W, a.vrows, a.H, mt * BM);
     lb.init(a.G + (int64_t)nt * 256 * a.ldg, (int64_t)a.grows - (int64_t)nt * 256, a.ldg);
-    gemm_tile<4, 4>(la, lb, (int)((a.vrows + kBK - 1) / kBK), st, acc);
+    gemm_tile<MI, 4>(la, lb, (int)((a.vrows + kBK - 1) / kBK), st, acc);
     out = a.dH;
     nvalid = a.rows;
     acc_mode = a.acc_dh;
@@ -869,31 +878,33 @@ __device__ __forceinline__ void bwd_tile(const BwdArgs& a, int L, Stages st) {
     const int id = xcd_remap(L - a.ndh_pad, a.ndw_pad);
     if (id >= a.ndw) return;
     grouped(id, a.nht, a.nvt, a.gm_dw, mt, nt);
-    LoaderKC<256> la;
-    LoaderTR lb;
-    la.init(a.hT + (int64_t)mt * 256 * a.ldt, a.H - (int64_t)mt * 256, a.ldt);
+    LoaderKC<BM> la;
+    LoaderTR<256> lb;
+    la.init(a.hT + (int64_t)mt * BM * a.ldt, a.H - (int64_t)mt * BM, a.ldt);
     lb.init(a.G, a.grows, a.ldg, nt * 256);
-    gemm_tile<4, 4>(la, lb, (int)((a.rows + kBK - 1) / kBK), st, acc);
+    gemm_tile<MI, 4>(la, lb, (int)((a.rows + kBK - 1) / kBK), st, acc);
     out = a.dW;
     nvalid = a.vrows;
     acc_mode = a.acc_dw;
   }
-  // The wave's 128 (m) x 128 (n) block leaves through a private 32 KiB LDS
-  // stage (free after gemm_tile), 64 columns n at a time: each lane writes its
-  // 4 consecutive m of one n (16-byte chunk m/4 of row n stored at position
-  // (m/4) ^ (n & 31), so the 32 columns of one write land in different
-  // banks), then every row n leaves as one 512-byte segment (32 lanes x 16
-  // bytes) instead of 32-byte pieces of 32 rows per store.  Accumulating
-  // reads the old values the same coalesced way (range-checked: zeros past
-  // the output's rows; past H within a row they are not stored).
+  // The wave's (32 MI) (m) x 128 (n) block leaves through a private 32 KiB
+  // LDS stage (free after gemm_tile), 64 columns n at a time: each lane
+  // writes its 4 consecutive m of one n (16-byte chunk m/4 of row n stored
+  // at position (m/4) ^ (n & 31), so the 32 columns of one write land in
+  // different banks), then every row n leaves as one segment of up to 512
+  // bytes (32 lanes x 16 bytes, the first 8 MI lanes holding the wave's m)
+  // instead of 32-byte pieces of 32 rows per store.  Accumulating reads the
+  // old values the same coalesced way (range-checked: zeros past the
+  // output's rows; lanes past the wave's m or past H read and store nothing).
   {
     const int w = threadIdx.x >> 6;
     float* stg = reinterpret_cast<float*>(w == 0 ? st.a0 : w == 1 ? st.a1 : w == 2 ? st.b0 : st.b1);
-    const int64_t m0 = (int64_t)mt * 256 + wm * 128;  // the wave's first m
-    const int64_t n0 = (int64_t)nt * 256 + wn * 128;  // the wave's first n
+    const int64_t m0 = (int64_t)mt * BM + wm * (32 * MI);  // the wave's first m
+    const int64_t n0 = (int64_t)nt * 256 + wn * 128;       // the wave's first n
     const __amdgpu_buffer_rsrc_t ro = make_rsrc(out, (uint64_t)nvalid * (uint64_t)a.H * 4u);
-    const int c = lane & 31;              // 16-byte chunk of a row: m = m0 + 4c .. 4c+3
-    const bool m_ok = m0 + 4 * c < a.H;   // H % 64 == 0: a chunk is all in or all out
+    const int c = lane & 31;  // 16-byte chunk of a row: m = m0 + 4c .. 4c+3
+    // H % 64 == 0: a chunk is all in or all out
+    const bool m_ok = c < 8 * MI && m0 + 4 * c < a.H;
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
 #pragma unroll
@@ -901,7 +912,7 @@ __device__ __forceinline__ void bwd_tile(const BwdArgs& a, int L, Stages st) {
         const int j = 2 * half + jj;
         const int nl = 32 * jj + (lane & 31);  // row of the stage
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < MI; ++i)
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const int ml = acc_row(i, 4 * q, lane);  // 4-aligned m within the wave's block
@@ -911,13 +922,15 @@ __device__ __forceinline__ void bwd_tile(const BwdArgs& a, int L, Stages st) {
       }
       __builtin_amdgcn_wave_barrier();
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      // rows r = 2k + (lane >> 5) of this half, k = 0..31
+      // rows r = 2k + (lane >> 5) of this half, k = 0..31; a lane with no m
+      // reads at an offset past every output (range check: zeros, no traffic)
       f32x4 old[32];
       if (acc_mode) {
 #pragma unroll
         for (int k = 0; k < 32; ++k) {
           const int64_t n = n0 + 64 * half + 2 * k + (lane >> 5);
-          old[k] = __builtin_bit_cast(f32x4, buf_load16(ro, (uint32_t)((n * a.H + m0 + 4 * c) * 4)));
+          const uint32_t off = m_ok ? (uint32_t)((n * a.H + m0 + 4 * c) * 4) : 0xFFFFFFF0u;
+          old[k] = __builtin_bit_cast(f32x4, buf_load16(ro, off));
         }
       }
 #pragma unroll
@@ -934,9 +947,14 @@ __device__ __forceinline__ void bwd_tile(const BwdArgs& a, int L, Stages st) {
   }
 }
 
+// Grid: [0, ndh_pad) dH work, then [ndh_pad, ndh_pad + ndw_pad) dW work;
+// inside each segment the 8 XCDs get contiguous work ranges (idle padding
+// workgroups exit at once).  dH tiles come first: their K loop (the chunk's
+// vocabulary) is the longer one.
+template <int MI>
 __global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) k_bwd(BwdArgs a) {
   KD_DECLARE_STAGES(st, 256, 256);
-  bwd_tile(a, blockIdx.x, st);
+  bwd_tile<MI>(a, blockIdx.x, st);
 }
 
 // The contractions of one (token block, vocabulary chunk) and the pass-2
@@ -944,12 +962,13 @@ __global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 
 // grid = k_bwd's grid, then p_pad (a multiple of 8) pass-2 workgroups.  The
 // dH tiles (longest) are dispatched first and the short pass-2 tiles last,
 // so they fill the contractions' uneven end instead of a launch boundary.
+template <int MI>
 __global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
 k_bwd_pass2(BwdArgs g, Pass2Args p, int p_pad) {
   KD_DECLARE_STAGES(st, 256, 256);
   const int nb = g.ndh_pad + g.ndw_pad;
   if ((int)blockIdx.x < nb) {
-    bwd_tile(g, blockIdx.x, st);
+    bwd_tile<MI>(g, blockIdx.x, st);
   } else {
     const int id = xcd_remap((int)blockIdx.x - nb, p_pad);
     if (id < p.total) pass2_tile(p, id, st);
