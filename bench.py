@@ -468,6 +468,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--seed", type=int, default=1)
     ap.add_argument("--workload", default="gptoss", choices=["gptoss", "long", "qwen", "tiny"])
+    ap.add_argument("--tokens", type=int, default=0,
+                    help="the gpt-oss head (H 2880, V 201088, K 64, tau 1) at this many tokens, as in the sweep")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-seq-chunk", action="store_true", help="skip the sequence-chunk schedule line")
     ap.add_argument("--no-variants", action="store_true", help="skip the logits / top-K variant lines")
@@ -497,7 +499,8 @@ def main():
             res.pop("roofline", None)
             print(json.dumps(res), flush=True)
         return
-    wl = synth.WORKLOADS[args.workload]
+    wl = (synth.Workload(f"sweep-T{args.tokens}", args.tokens, 2880, 201088, 64, 1.0) if args.tokens
+          else synth.WORKLOADS[args.workload])
     res, x = run_one(args, wl)
     res["config"]["schedule"] = "recompute (pass 2 recomputes each vocabulary chunk)"
     if not args.no_seq_chunk:
@@ -511,7 +514,7 @@ def main():
     else:
         res["cpu_baseline"] = None
     del x
-    if not args.no_scaling and args.workload == "gptoss":
+    if not args.no_scaling and args.workload == "gptoss" and not args.tokens:
         res["scaling"] = scaling_lines(args)
     print(json.dumps(res), flush=True)
 
