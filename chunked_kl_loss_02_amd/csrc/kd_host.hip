@@ -5,6 +5,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <atomic>
 #include <mutex>
 #include <vector>
 
@@ -186,8 +187,12 @@ struct TimedLaunch {
   int cls;
   hipEvent_t a, b;
 };
-bool g_timing = false;
-uint32_t g_timing_mask = ~0u;
+// The optional timing facility's state, shared by every caller thread:
+// g_timing / g_timing_mask are read without the lock on each launch (a
+// torn read only times a launch more or less), the event lists under it.
+std::atomic<bool> g_timing{false};
+std::atomic<uint32_t> g_timing_mask{~0u};
+std::mutex g_timing_mu;
 constexpr int kTimingClasses = 12;
 std::vector<TimedLaunch> g_launches;
 std::vector<hipEvent_t> g_pool;
@@ -210,8 +215,10 @@ struct Launcher {
   void run(int cls, F&& f) {
     if (err != hipSuccess) return;
     hipEvent_t a = nullptr, b = nullptr;
-    const bool timed = g_timing && ((g_timing_mask >> cls) & 1u);
+    const bool timed = g_timing.load(std::memory_order_relaxed) &&
+                       ((g_timing_mask.load(std::memory_order_relaxed) >> cls) & 1u);
     if (timed) {
+      std::lock_guard<std::mutex> lock(g_timing_mu);
       a = pool_get();
       b = pool_get();
       if (a) (void)hipEventRecord(a, s);
@@ -221,6 +228,7 @@ struct Launcher {
     if (e != hipSuccess) err = e;
     if (timed && a && b) {
       (void)hipEventRecord(b, s);
+      std::lock_guard<std::mutex> lock(g_timing_mu);
       g_launches.push_back({cls, a, b});
     }
   }
@@ -818,16 +826,17 @@ const float* kd_topk_kl_workspace_lse2(const kd_problem* p, const void* workspac
 }
 
 kd_status kd_timing_enable(int on) {
-  g_timing = on != 0;
+  g_timing.store(on != 0);
   return KD_OK;
 }
 
 kd_status kd_timing_classes(uint32_t mask) {
-  g_timing_mask = mask;
+  g_timing_mask.store(mask);
   return KD_OK;
 }
 
 kd_status kd_timing_collect(double* ms, int64_t* launches) {
+  std::lock_guard<std::mutex> lock(g_timing_mu);
   kd_status st = KD_OK;
   for (auto& l : g_launches) {
     if (hipEventSynchronize(l.b) != hipSuccess) st = KD_ERR_HIP;

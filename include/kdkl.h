@@ -52,7 +52,10 @@ typedef enum kd_status {
   KD_ERR_WORKSPACE = 3,    /* workspace_bytes smaller than kd_topk_kl_workspace_size() */
   KD_ERR_INDEX = 4,        /* (KD_FLAG_VALIDATE) a kept row has a teacher id outside [0, V) */
   KD_ERR_NONFINITE = 5,    /* (KD_FLAG_VALIDATE) a kept row has a NaN/+inf logit or all -inf */
-  KD_ERR_HIP = 6           /* a HIP runtime call failed (no device, launch failure ...) */
+  KD_ERR_HIP = 6,          /* a HIP runtime call failed (no device, launch failure ...) */
+  /* not a status: gives the enum the value range of int32_t, so any code
+   * handed back to kd_status_string is a valid kd_status value in C++ too */
+  KD_STATUS_RANGE_ = INT32_MIN
 } kd_status;
 
 /* Check teacher ids and logits of kept rows on the device, then synchronise
@@ -275,7 +278,8 @@ int kd_abi_version(void);
 
 /* Optional per-kernel timing with HIP events recorded on the launch stream
  * around every launch of the library's kernels while enabled.  Intended for
- * benchmarks; not thread-safe.  Kernel classes: 0 teacher, 1 gather,
+ * benchmarks; the state is process-wide (calls from several threads add
+ * their launches to one list, under a lock).  Kernel classes: 0 teacher, 1 gather,
  * 2 pass1, 3 lse, 4 loss, 5 pass2, 6 fixup (the teacher-entry buckets or
  * the dense fixup), 7 bwd, 8 other, 9 logits (the row kernel of
  * kd_topk_kl_logits), 10 topk (kd_topk_select), 11 bwd_pass2 (one unit's
