@@ -87,21 +87,16 @@ struct LoaderKC {
   }
 };
 
-// Loader for a tile of COLS (256 or 192) rows x 64 k of a row-contiguous
-// operand (element (row, k) at base + k*ld + row: W or h or G contracted
-// over their leading index), global -> LDS without registers and without a
-// transpose: the stage holds the 64 k-rows as they are in memory ([64][256]
-// bf16, 512 B per row), and the MFMA fragments are read with
-// ds_read_b64_tr_b16, which hands lane i of each 16-lane group 4
-// consecutive k of column i from the 4 rows its group addresses.  16-byte
-// chunk c of k-row r sits at position c ^ kTrMask[r & 3]; the masks
-// {0, 6, 10, 12} put the 4 rows x 2 (or 4) chunks of one transposed read in
-// distinct bank groups.  With COLS = 192 the positions of chunks 24..31 are
-// never read; the lanes that fill them fetch chunk c - 8 instead, a line
-// the same instruction fetches anyway, so no bytes are added.
-template <int COLS = 256>
+// Loader for a tile of 256 rows x 64 k of a row-contiguous operand (element
+// (row, k) at base + k*ld + row: W or h or G contracted over their leading
+// index), global -> LDS without registers and without a transpose: the stage
+// holds the 64 k-rows as they are in memory ([64][256] bf16, 512 B per row),
+// and the MFMA fragments are read with ds_read_b64_tr_b16, which hands lane
+// i of each 16-lane group 4 consecutive k of column i from the 4 rows its
+// group addresses.  16-byte chunk c of k-row r sits at position
+// c ^ kTrMask[r & 3]; the masks {0, 6, 10, 12} put the 4 rows x 2 (or 4)
+// chunks of one transposed read in distinct bank groups.
 struct LoaderTR {
-  static_assert(COLS == 256 || COLS == 192, "transposed tile width");
   static constexpr int NQ = 8;       // 64 rows x 512 B = 32 KiB = 8 x 1 KiB per wave
   static constexpr int kVmem = NQ;
   static constexpr int kReads = 2;
@@ -123,8 +118,7 @@ struct LoaderTR {
 #pragma unroll
     for (int j = 0; j < NQ; ++j) {
       const int r = 2 * (w * NQ + j) + (lane >> 5);  // k-row of the stage
-      int c = (lane & 31) ^ trm(r);                 // logical chunk landing in this lane's slot
-      if (c >= COLS / 8) c -= 8;                    // an unread slot (COLS = 192)
+      const int c = (lane & 31) ^ trm(r);           // logical chunk landing in this lane's slot
       voff[j] = (uint32_t)r * ldb + (uint32_t)row0 * 2u + (uint32_t)c * 16u;
     }
   }

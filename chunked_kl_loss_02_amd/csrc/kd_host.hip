@@ -132,9 +132,6 @@ Plan make_plan(const kd_problem* p, bool with_grad = true, bool one_gbuf = false
   P.gv2 = env_int("KDKL_GROUP_V2", 8);
   P.gm_dh = std::max(1, env_int("KDKL_GROUP_MDH", 6));
   P.gm_dw = std::max(1, env_int("KDKL_GROUP_MDW", 4));
-  // 256-row contraction tiles: at H = 2880 the last one holds 64 rows, but
-  // 192-row tiles (2880 = 15 x 192, bitwise the same results) measured
-  // slower (one fourth more fragment reads and loads per flop)
   P.bm = 256;
   if (P.gt1 < 1) P.gt1 = 1;
   if (P.gt2 < 1) P.gt2 = 1;
@@ -417,7 +414,7 @@ void launch_transpose_h(Launcher& L, const Plan& P, const Inputs& in, const Bufs
 // The gradient contractions of one unit alone (k_bwd at the plan's tile height).
 void launch_bwd(Launcher& L, const Plan& P, const kd::BwdArgs& g, int grid) {
   hipStream_t s = L.s;
-  L.run(7, [&] { kd::k_bwd<4><<<grid, 256, 0, s>>>(g); });
+  L.run(7, [&] { kd::k_bwd<<<grid, 256, 0, s>>>(g); });
 }
 
 // Pass 2: for each token block (outer) and vocabulary chunk (inner),
@@ -535,7 +532,7 @@ void launch_backward(Launcher& L, const Plan& P, uint32_t flags, const Inputs& i
     } else if (i + 1 < units.size()) {
       const Pass2Args& pn = units[i + 1].p;
       const int p_pad = pad8(pn.total);
-      L.run(11, [&] { k_bwd_pass2<4><<<nb + p_pad, 256, 0, s>>>(u.g, pn, p_pad); });
+      L.run(11, [&] { k_bwd_pass2<<<nb + p_pad, 256, 0, s>>>(u.g, pn, p_pad); });
     } else {
       launch_bwd(L, P, u.g, nb);
     }

@@ -848,14 +848,12 @@ struct BwdArgs {
   int acc_dh, acc_dw;     // accumulate (1) or overwrite (0)
 };
 
-// One gradient-contraction workgroup, linear id L of the k_bwd grid.  The
-// output tile is (64 MI) hidden units x 256: MI = 4 (256 rows), or MI = 3
-// (192 rows, for hidden sizes that 192 divides and 256 does not, e.g.
-// 2880 = 15 x 192, where 256-row tiles would leave a quarter-full last
-// tile of zero rows in every contraction).
-template <int MI>
+// One gradient-contraction workgroup, linear id L of the k_bwd grid: a
+// 256 (hidden) x 256 output tile.  (At H = 2880 the last hidden tile holds
+// 64 valid rows; 192-row tiles, 2880 = 15 x 192, gave bitwise the same
+// results but ran slower: a fourth more fragment reads and loads per flop.)
 __device__ __forceinline__ void bwd_tile(const BwdArgs& a, int L, Stages st) {
-  constexpr int BM = 64 * MI;  // hidden rows of the tile
+  constexpr int MI = 4, BM = 256;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int wm = w & 1, wn = w >> 1;
   f32x16 acc[MI][4];
@@ -866,7 +864,7 @@ __device__ __forceinline__ void bwd_tile(const BwdArgs& a, int L, Stages st) {
     const int id = xcd_remap(L, a.ndh_pad);
     if (id >= a.ndh) return;
     grouped(id, a.nht, a.ntt, a.gm_dh, mt, nt);
-    LoaderTR<BM> la;
+    LoaderTR la;
     LoaderKC<256> lb;
     la.init(a.W, a.vrows, a.H, mt * BM);
     lb.init(a.G + (int64_t)nt * 256 * a.ldg, (int64_t)a.grows - (int64_t)nt * 256, a.ldg);
@@ -879,7 +877,7 @@ __device__ __forceinline__ void bwd_tile(const BwdArgs& a, int L, Stages st) {
     if (id >= a.ndw) return;
     grouped(id, a.nht, a.nvt, a.gm_dw, mt, nt);
     LoaderKC<BM> la;
-    LoaderTR<256> lb;
+    LoaderTR lb;
     la.init(a.hT + (int64_t)mt * BM * a.ldt, a.H - (int64_t)mt * BM, a.ldt);
     lb.init(a.G, a.grows, a.ldg, nt * 256);
     gemm_tile<MI, 4>(la, lb, (int)((a.rows + kBK - 1) / kBK), st, acc);
@@ -951,10 +949,9 @@ __device__ __forceinline__ void bwd_tile(const BwdArgs& a, int L, Stages st) {
 // inside each segment the 8 XCDs get contiguous work ranges (idle padding
 // workgroups exit at once).  dH tiles come first: their K loop (the chunk's
 // vocabulary) is the longer one.
-template <int MI>
 __global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) k_bwd(BwdArgs a) {
   KD_DECLARE_STAGES(st, 256, 256);
-  bwd_tile<MI>(a, blockIdx.x, st);
+  bwd_tile(a, blockIdx.x, st);
 }
 
 // The contractions of one (token block, vocabulary chunk) and the pass-2
@@ -962,13 +959,12 @@ __global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 
 // grid = k_bwd's grid, then p_pad (a multiple of 8) pass-2 workgroups.  The
 // dH tiles (longest) are dispatched first and the short pass-2 tiles last,
 // so they fill the contractions' uneven end instead of a launch boundary.
-template <int MI>
 __global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
 k_bwd_pass2(BwdArgs g, Pass2Args p, int p_pad) {
   KD_DECLARE_STAGES(st, 256, 256);
   const int nb = g.ndh_pad + g.ndw_pad;
   if ((int)blockIdx.x < nb) {
-    bwd_tile<MI>(g, blockIdx.x, st);
+    bwd_tile(g, blockIdx.x, st);
   } else {
     const int id = xcd_remap((int)blockIdx.x - nb, p_pad);
     if (id < p.total) pass2_tile(p, id, st);
