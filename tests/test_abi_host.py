@@ -256,3 +256,18 @@ def test_noalloc_rejects_problems_beyond_its_scratch_before_any_hip_call():
     bad = kd.problem(16, 64, 100, 4, tau=0.0)
     assert L.kd_topk_kl_fwd_bwd_noalloc(ctypes.byref(bad), fake, fake, fake, fake, vp(0), fake, fake, fake,
                                         vp(0), vp(0)) == 1
+
+
+def test_tiling_query_reports_the_default_plan():
+    # one token block: 12288-row chunks, two gradient buffers (several units)
+    assert kd.tiling(4096, 2880, 201088, 64) == (4096, 12288, 2)
+    # blocks of 8192 above 4096 tokens take 8192-row chunks
+    assert kd.tiling(16384, 2880, 201088, 64) == (8192, 8192, 2)
+    # T below one block: the block is T rounded up to 256
+    assert kd.tiling(1000, 2880, 201088, 64) == (1024, 12288, 2)
+    # a single (block, chunk) unit needs one buffer
+    assert kd.tiling(1000, 256, 4096, 32, chunk_v=4096) == (1024, 4096, 1)
+    # the sequence-chunk schedule: blocks of 4096, chunks of 16384, one buffer
+    assert kd.tiling(16384, 2880, 201088, 64, seq_chunk=True) == (4096, 16384, 1)
+    # the caller's tiling wins
+    assert kd.tiling(16384, 2880, 201088, 64, chunk_v=4096, block_t=2048) == (2048, 4096, 2)
