@@ -84,3 +84,31 @@ def test_noalloc_refuses_a_problem_beyond_its_scratch():
     with pytest.raises(kd.KdError) as e:
         kd.fwd_bwd_noalloc(h, W, idx, lg, m, 1.0, out=out, chunk_v=262144)
     assert e.value.code == 3
+
+
+def test_noalloc_call_replays_in_a_graph():
+    # the callers it is for: code under graph capture.  The first call on the
+    # GPU resolves the scratch address, outside the capture
+    print("[noalloc] graph capture", flush=True)
+    x = synth.make_inputs_torch(600, 256, 5000, 16, seed=22, mask="packed8")
+    args = (x["h"], x["W"], x["teacher_idx"], x["teacher_logit"], x["mask"], 1.5)
+    kw = dict(chunk_v=1024, block_t=256, row_loss=True)
+    out = (torch.empty((), device="cuda"), torch.empty((600, 256), device="cuda"),
+           torch.empty((5000, 256), device="cuda"), torch.empty((600,), device="cuda"))
+    kd.fwd_bwd_noalloc(*args, out=out, **kw)
+    torch.cuda.synchronize()
+    eager = [t.clone() for t in out]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        kd.fwd_bwd_noalloc(*args, out=out, **kw)
+    torch.cuda.synchronize()
+    for r in range(3):
+        other = kd.fwd_bwd(*args, **kw)  # eager work between replays
+        torch.cuda.synchronize()
+        for t in out:
+            t.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        for name, a, b, c in zip(("loss", "dH", "dW", "row_loss"), out, eager, other):
+            assert torch.equal(a, b), (r, name)
+            assert torch.equal(c, b), (r, name)
