@@ -49,6 +49,11 @@ struct Plan {
   int gv1, gv2;      // vocabulary group sizes (take precedence when > 0)
   int gm_dh, gm_dw;  // hidden-tile group sizes of the gradient contractions
   int bm;            // hidden rows of a gradient-contraction tile
+  // the last hidden tile's height in 64-row units when H % 256 is 64 or 128
+  // (else 0: a full tile), and the pitch of the copy of W's last columns
+  // that its dH tiles read
+  int rem_mi;
+  int64_t ldwr;
   int64_t ldp;       // leading dim of the pass-1 partials
   int64_t grows;     // rows of the gradient buffer
   int64_t nunits;    // (token block, vocabulary chunk) units of the gradient pass
@@ -59,6 +64,7 @@ struct Plan {
   bool seq;          // sequence-chunk schedule (stored logits of a token block)
   size_t o_S;        // seq: S^T of one block, [V, Tb] fp32
   size_t o_hT;       // h^T of one token block, [H, Tb] bf16 (gradient pass)
+  size_t o_wtr;      // W's last 64 rem_mi columns, [64 rem_mi, ldwr] bf16 (gradient pass)
   size_t o_off;      // per-token pass-2 offsets [Tp] (gradient pass)
   // teacher entries by (token tile, vocabulary tile): counts / starts
   // [ntt_all, ldk] then fill cursors [ntt_all, ldk] (contiguous, cleared
@@ -133,6 +139,13 @@ Plan make_plan(const kd_problem* p, bool with_grad = true, bool one_gbuf = false
   P.gm_dh = std::max(1, env_int("KDKL_GROUP_MDH", 6));
   P.gm_dw = std::max(1, env_int("KDKL_GROUP_MDW", 4));
   P.bm = 256;
+  // a 64- or 128-row last hidden tile (the copy's 32-bit offsets permitting;
+  // not in the allocation-free entry point's plan, which keeps full-height
+  // tiles and no copy: the results are bitwise the same, the k order of
+  // every dot product being unchanged)
+  P.ldwr = (P.V + 63) / 64 * 64;
+  const int64_t rem = P.H % 256;
+  P.rem_mi = !one_gbuf && (rem == 64 || rem == 128) && rem * P.ldwr * 2 <= (int64_t)UINT32_MAX ? (int)(rem / 64) : 0;
   if (P.gt1 < 1) P.gt1 = 1;
   if (P.gt2 < 1) P.gt2 = 1;
   P.ldp = (int64_t)P.ntt_max * 256;
@@ -147,6 +160,7 @@ Plan make_plan(const kd_problem* p, bool with_grad = true, bool one_gbuf = false
   P.ngbuf = !P.seq && !one_gbuf && P.nunits > 1 ? 2 : 1;
   P.o_G = with_grad ? take((size_t)P.ngbuf * P.grows * P.chunk_v * 2) : 0;
   P.o_hT = with_grad ? take((size_t)P.H * P.Tb * 2) : 0;
+  P.o_wtr = with_grad && P.rem_mi ? take((size_t)64 * P.rem_mi * P.ldwr * 2) : 0;
   P.o_off = with_grad ? take((size_t)Tp * 4) : 0;
   P.ntt_all = (int)cdiv(P.T, 256);
   P.ldk = (int)P.nvt + 1;
@@ -246,6 +260,7 @@ struct Inputs {
 struct Bufs {
   uint16_t* G;
   uint16_t* hT;  // h^T of one token block (gradient pass)
+  uint16_t* wtr;  // W's last columns, k-contiguous (gradient pass, nullable)
   float* off;    // pass-2 offsets (gradient pass)
   uint32_t *bcnt, *bcur, *bbase, *ent, *enti;  // teacher entries by tile
   float* dhs;   // fp32 staging of a bf16 dH (nullable)
@@ -268,6 +283,7 @@ Bufs carve(const Plan& P, void* workspace, bool with_grad) {
   Bufs b{};
   b.G = with_grad ? reinterpret_cast<uint16_t*>(ws + P.o_G) : nullptr;
   b.hT = with_grad ? reinterpret_cast<uint16_t*>(ws + P.o_hT) : nullptr;
+  b.wtr = with_grad && P.rem_mi ? reinterpret_cast<uint16_t*>(ws + P.o_wtr) : nullptr;
   b.off = with_grad ? reinterpret_cast<float*>(ws + P.o_off) : nullptr;
   b.bcnt = reinterpret_cast<uint32_t*>(ws + P.o_bcnt);
   b.bcur = reinterpret_cast<uint32_t*>(ws + P.o_bcur);
@@ -411,6 +427,16 @@ void launch_transpose_h(Launcher& L, const Plan& P, const Inputs& in, const Bufs
   L.run(8, [&] { kd::k_transpose_h<<<grid, 256, 0, s>>>(in.h + t0 * P.H, rows, P.H, b.hT, P.Tb); });
 }
 
+// The k-contiguous copy of W's last 64 rem_mi columns that the dH tiles of
+// the last hidden tile read: wtr[j, v] = W[v, H - 64 rem_mi + j], zero for
+// V <= v < ldwr (k_transpose_h over those columns).
+void launch_transpose_wrem(Launcher& L, const Plan& P, const Inputs& in, const Bufs& b) {
+  hipStream_t s = L.s;
+  const int64_t c0 = P.H - 64 * P.rem_mi;
+  const dim3 grid((unsigned)(P.ldwr / 64), (unsigned)P.rem_mi);
+  L.run(8, [&] { kd::k_transpose_h<<<grid, 256, 0, s>>>(in.W + c0, P.V, P.H, b.wtr, P.ldwr); });
+}
+
 // The gradient contractions of one unit alone (k_bwd at the plan's tile height).
 void launch_bwd(Launcher& L, const Plan& P, const kd::BwdArgs& g, int grid) {
   hipStream_t s = L.s;
@@ -442,6 +468,7 @@ void launch_backward(Launcher& L, const Plan& P, uint32_t flags, const Inputs& i
   });
   if (!have_index) launch_bucket_index(L, P, in, b);
   launch_bucket_value(L, P, b);
+  if (dH_out && P.rem_mi) launch_transpose_wrem(L, P, in, b);
   struct Unit {
     int64_t t0, rows, v0, vrows;
     int bi, ci;
@@ -508,6 +535,9 @@ void launch_backward(Launcher& L, const Plan& P, uint32_t flags, const Inputs& i
       g.gm_dw = std::min(P.gm_dw, nht);
       g.ldg = P.chunk_v;
       g.grows = (int)P.grows;
+      g.rem_mi = P.rem_mi;
+      g.WTr = b.wtr ? b.wtr + v0 : nullptr;
+      g.ldwr = P.ldwr;
       // the first contribution overwrites, later ones add; a caller's
       // accumulate flag makes every fp32 contribution add (bf16 outputs add
       // in the final rounding instead)
@@ -573,6 +603,7 @@ void launch_seq(Launcher& L, const Plan& P, uint32_t flags, const Inputs& in, co
   const bool whole_dw = T > P.Tb;  // bf16 staging holds all of dW
   const int nht = (int)cdiv(H, P.bm);
   const int64_t lds = P.Tb;
+  if (dH_out && P.rem_mi) launch_transpose_wrem(L, P, in, b);
   int bi = 0;
   for (int64_t t0 = 0; t0 < T; t0 += P.Tb, ++bi) {
     const int64_t rows = std::min<int64_t>(P.Tb, T - t0);
@@ -650,6 +681,9 @@ void launch_seq(Launcher& L, const Plan& P, uint32_t flags, const Inputs& in, co
       g.gm_dw = std::min(P.gm_dw, nht);
       g.ldg = P.chunk_v;
       g.grows = (int)P.grows;
+      g.rem_mi = P.rem_mi;
+      g.WTr = b.wtr ? b.wtr + v0 : nullptr;
+      g.ldwr = P.ldwr;
       g.acc_dh = ci > 0 || (acc_dh_in && !bf16);
       g.acc_dw = bi > 0 || (acc_dw_in && !bf16);
       launch_bwd(L, P, g, g.ndh_pad + g.ndw_pad);

@@ -83,7 +83,9 @@ __global__ void k_to_bf16(const float* __restrict__ src, uint16_t* __restrict__ 
 __device__ __forceinline__ void lse_merge(float& m, float& l, float om, float ol) {
   const float nm = fmaxf(m, om);
   if (nm == -INFINITY) return;
-  l = l * fast_exp2(m - nm) + ol * fast_exp2(om - nm);
+  // one rounding order wherever this is inlined: an explicit fma, not a
+  // contraction the compiler may place on either product
+  l = fmaf(l, fast_exp2(m - nm), ol * fast_exp2(om - nm));
   m = nm;
 }
 
@@ -846,37 +848,49 @@ struct BwdArgs {
   int ndh_pad, ndw_pad;   // segment sizes rounded up to multiples of 8
   int gm_dh, gm_dw;       // hidden-tile group sizes of the two rasters
   int acc_dh, acc_dw;     // accumulate (1) or overwrite (0)
+  // The last hidden tile when H % 256 is 64 or 128: rem_mi (1 or 2) 32-row
+  // subtiles per wave instead of 4 (a 64 or 128-row tile, all rows valid),
+  // else 0 (a full 256-row tile, its rows past H computed and dropped).  Its
+  // dH tiles read W's last 64 rem_mi columns from WTr, a k-contiguous copy
+  // ([64 rem_mi, ldwr], chunk origin, zero past V; k_transpose_h of W).
+  int rem_mi;
+  const uint16_t* WTr;
+  int64_t ldwr;
 };
 
-// One gradient-contraction workgroup, linear id L of the k_bwd grid: a
-// 256 (hidden) x 256 output tile.  (At H = 2880 the last hidden tile holds
-// 64 valid rows; 192-row tiles, 2880 = 15 x 192, gave bitwise the same
-// results but ran slower: a fourth more fragment reads and loads per flop.)
-__device__ __forceinline__ void bwd_tile(const BwdArgs& a, int L, Stages st) {
-  constexpr int MI = 4, BM = 256;
+// One gradient-contraction tile: hidden tile mt (rows mt * 256 ...) by token
+// tile (dH) or vocabulary tile (dW) nt, 64 MI hidden rows (MI = 4: the full
+// 256; fewer for the last tile of an H that is not a multiple of 256).
+// (At H = 2880, 192-row tiles throughout, 2880 = 15 x 192, gave bitwise the
+// same results but ran slower: a fourth more fragment reads and loads per
+// flop.)
+template <int MI>
+__device__ __forceinline__ void bwd_contract(const BwdArgs& a, bool dh, int mt, int nt, Stages st) {
+  constexpr int BM = 256;  // hidden-tile pitch
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int wm = w & 1, wn = w >> 1;
   f32x16 acc[MI][4];
   float* out;
   int64_t nvalid;
-  int mt, nt, acc_mode;
-  if (L < a.ndh_pad) {
-    const int id = xcd_remap(L, a.ndh_pad);
-    if (id >= a.ndh) return;
-    grouped(id, a.nht, a.ntt, a.gm_dh, mt, nt);
-    LoaderTR la;
+  int acc_mode;
+  if (dh) {
     LoaderKC<256> lb;
-    la.init(a.W, a.vrows, a.H, mt * BM);
     lb.init(a.G + (int64_t)nt * 256 * a.ldg, (int64_t)a.grows - (int64_t)nt * 256, a.ldg);
-    gemm_tile<MI, 4>(la, lb, (int)((a.vrows + kBK - 1) / kBK), st, acc);
+    const int nk = (int)((a.vrows + kBK - 1) / kBK);
+    if constexpr (MI == 4) {
+      LoaderTR la;
+      la.init(a.W, a.vrows, a.H, mt * BM);
+      gemm_tile<MI, 4>(la, lb, nk, st, acc);
+    } else {
+      LoaderKC<64 * MI> la;
+      la.init(a.WTr, a.H - (int64_t)mt * BM, a.ldwr);
+      gemm_tile<MI, 4>(la, lb, nk, st, acc);
+    }
     out = a.dH;
     nvalid = a.rows;
     acc_mode = a.acc_dh;
   } else {
-    const int id = xcd_remap(L - a.ndh_pad, a.ndw_pad);
-    if (id >= a.ndw) return;
-    grouped(id, a.nht, a.nvt, a.gm_dw, mt, nt);
-    LoaderKC<BM> la;
+    LoaderKC<64 * MI> la;
     LoaderTR lb;
     la.init(a.hT + (int64_t)mt * BM * a.ldt, a.H - (int64_t)mt * BM, a.ldt);
     lb.init(a.G, a.grows, a.ldg, nt * 256);
@@ -943,6 +957,30 @@ __device__ __forceinline__ void bwd_tile(const BwdArgs& a, int L, Stages st) {
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     }
   }
+}
+
+// The gradient-contraction workgroup with linear id L of the k_bwd grid.
+__device__ __forceinline__ void bwd_tile(const BwdArgs& a, int L, Stages st) {
+  int mt, nt;
+  bool dh;
+  if (L < a.ndh_pad) {
+    const int id = xcd_remap(L, a.ndh_pad);
+    if (id >= a.ndh) return;
+    grouped(id, a.nht, a.ntt, a.gm_dh, mt, nt);
+    dh = true;
+  } else {
+    const int id = xcd_remap(L - a.ndh_pad, a.ndw_pad);
+    if (id >= a.ndw) return;
+    grouped(id, a.nht, a.nvt, a.gm_dw, mt, nt);
+    dh = false;
+  }
+  const int mi = mt == a.nht - 1 ? a.rem_mi : 0;
+  if (mi == 1)
+    bwd_contract<1>(a, dh, mt, nt, st);
+  else if (mi == 2)
+    bwd_contract<2>(a, dh, mt, nt, st);
+  else
+    bwd_contract<4>(a, dh, mt, nt, st);
 }
 
 // Grid: [0, ndh_pad) dH work, then [ndh_pad, ndh_pad + ndw_pad) dW work;

@@ -26,7 +26,9 @@
  * the caller's workspace (see kd_topk_kl_workspace_size): two fixed
  * block_t x chunk_v bf16 gradient buffers (one when the call has a single
  * token block and vocabulary chunk), h^T of one token block (H x block_t
- * bf16) plus O(T*K + T*V/256) per-token state.  It allocates no device
+ * bf16), when H % 256 is 64 or 128 a copy of W's last H % 256 columns
+ * ((H % 256) x V bf16, rounded up to 64 columns of V), plus
+ * O(T*K + T*V/256) per-token state.  It allocates no device
  * memory, keeps no state between calls (except the optional timing
  * facility below and the static scratch of kd_topk_kl_fwd_bwd_noalloc) and
  * is reentrant across streams given distinct workspaces.

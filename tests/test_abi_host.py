@@ -52,9 +52,10 @@ def test_workspace_plan():
     code, n = _ws(4096, 2880, 201088, 64)
     assert code == 0
     # two gradient buffers (4096 x 12288 bf16: one unit's contractions run
-    # beside the next unit's pass 2), the block's h^T (2880 x 4096 bf16) plus
-    # per-token state
-    fixed = 2 * 4096 * 12288 * 2 + 2880 * 4096 * 2
+    # beside the next unit's pass 2), the block's h^T (2880 x 4096 bf16), the
+    # k-contiguous copy of W's last 64 columns (2880 = 11 x 256 + 64: the last
+    # hidden tile of the contractions is 64 rows high) plus per-token state
+    fixed = 2 * 4096 * 12288 * 2 + 2880 * 4096 * 2 + 64 * 201088 * 2
     assert fixed <= n < fixed + 4096 * 8 * 1024
     # per-token growth is linear once T exceeds one block
     _, a = _ws(65536, 2880, 201088, 64)
@@ -158,9 +159,10 @@ def test_split_entry_point_sizes():
     assert code == 0
     code, fwd = _size(L.kd_topk_kl_fwd_workspace_size, T, H, V, K)
     assert code == 0
-    # the forward needs no gradient buffers (2 x 4096 x 12288 bf16), no h^T (2880 x 4096 bf16)
-    # and no per-token pass-2 offsets (4096 fp32); both bucket the teacher entries by tile
-    assert full - fwd == 2 * 4096 * 12288 * 2 + H * 4096 * 2 + 4 * 4096
+    # the forward needs no gradient buffers (2 x 4096 x 12288 bf16), no h^T (2880 x 4096 bf16),
+    # no copy of W's last 64 columns (64 x 201088 bf16) and no per-token pass-2 offsets
+    # (4096 fp32); both bucket the teacher entries by tile
+    assert full - fwd == 2 * 4096 * 12288 * 2 + H * 4096 * 2 + 64 * V * 2 + 4 * 4096
     code, saved = _size(L.kd_topk_kl_saved_size, T, H, V, K)
     assert code == 0
     # log-sum-exp [T] and the gathered logits [T, K], fp32, 256-byte aligned pieces
@@ -248,9 +250,11 @@ def test_noalloc_rejects_problems_beyond_its_scratch_before_any_hip_call():
     assert _ws(4096, 2880, 201088, 64)[1] > kd.NOALLOC_SCRATCH_BYTES
     assert L.kd_topk_kl_fwd_bwd_noalloc(ctypes.byref(p), fake, fake, fake, fake, vp(0), fake, fake, fake,
                                         vp(0), vp(0)) == 3
-    # with 8192-row chunks its single-buffer plan (one 4096 x 8192 bf16 gradient buffer
-    # less than kd_topk_kl_workspace_size) fits (checked on the GPU); argument errors come first
-    assert _ws(4096, 2880, 201088, 64, 1.0, 8192, 0)[1] - 4096 * 8192 * 2 <= kd.NOALLOC_SCRATCH_BYTES
+    # with 8192-row chunks its single-buffer plan (one 4096 x 8192 bf16 gradient buffer and the
+    # copy of W's last 64 columns less than kd_topk_kl_workspace_size) fits (checked on the GPU);
+    # argument errors come first
+    assert _ws(4096, 2880, 201088, 64, 1.0, 8192, 0)[1] - 4096 * 8192 * 2 - 64 * 201088 * 2 <= \
+        kd.NOALLOC_SCRATCH_BYTES
     assert L.kd_topk_kl_fwd_bwd_noalloc(ctypes.byref(p), fake, vp(0), fake, fake, vp(0), fake, fake, fake,
                                         vp(0), vp(0)) == 1
     bad = kd.problem(16, 64, 100, 4, tau=0.0)
