@@ -157,7 +157,7 @@ Plan make_plan(const kd_problem* p, bool with_grad = true, bool one_gbuf = false
   // several (block, chunk) units (the next unit's pass 2 runs beside the
   // current unit's contractions)
   P.nunits = cdiv(P.T, P.Tb) * cdiv(P.V, P.chunk_v);
-  P.ngbuf = !P.seq && !one_gbuf && P.nunits > 1 ? 2 : 1;
+  P.ngbuf = !one_gbuf && (P.seq ? P.V > P.chunk_v : P.nunits > 1) ? 2 : 1;
   P.o_G = with_grad ? take((size_t)P.ngbuf * P.grows * P.chunk_v * 2) : 0;
   P.o_hT = with_grad ? take((size_t)P.H * P.Tb * 2) : 0;
   P.o_wtr = with_grad && P.rem_mi ? take((size_t)64 * P.rem_mi * P.ldwr * 2) : 0;
@@ -364,7 +364,7 @@ void launch_bucket_value(Launcher& L, const Plan& P, const Bufs& b) {
   using namespace kd;
   const int64_t n = P.T * P.K;
   L.run(6, [&] {
-    k_bucket_value<<<(unsigned)cdiv(n, 256), 256, 0, s>>>(b.s, b.pm, b.lse2, b.scal_f, P.K, kLog2e / P.tau,
+    k_bucket_value<<<(unsigned)cdiv(n, 256), 256, 0, s>>>(b.s, b.pm, b.lse2, b.scal_f, P.K, kLog2e / P.tau, b.bbase,
                                                           b.bbase + P.ntt_all, b.enti, b.ent);
   });
 }
@@ -603,6 +603,7 @@ void launch_seq(Launcher& L, const Plan& P, uint32_t flags, const Inputs& in, co
   const bool whole_dw = T > P.Tb;  // bf16 staging holds all of dW
   const int nht = (int)cdiv(H, P.bm);
   const int64_t lds = P.Tb;
+  if (dH_out || dW_out) launch_bucket_index(L, P, in, b);
   if (dH_out && P.rem_mi) launch_transpose_wrem(L, P, in, b);
   int bi = 0;
   for (int64_t t0 = 0; t0 < T; t0 += P.Tb, ++bi) {
@@ -635,36 +636,59 @@ void launch_seq(Launcher& L, const Plan& P, uint32_t flags, const Inputs& in, co
                                                                b.s + t0 * K);
     });
     if (!dH_out && !dW_out) continue;
+    // the block's teacher entries get their gradient values (its logits
+    // at the cached ids and its lse2 are final now)
+    L.run(6, [&] {
+      k_bucket_value<<<(unsigned)cdiv(rows * K, 256), 256, 0, s>>>(b.s, b.pm, b.lse2, b.scal_f, K, c,
+                                                                   b.bbase + t0 / 256, b.bbase + t0 / 256 + ntt,
+                                                                   b.enti, b.ent);
+    });
     if (dW_out) launch_transpose_h(L, P, in, b, t0, rows);
-    int ci = 0;
-    for (int64_t v0 = 0; v0 < V; v0 += P.chunk_v, ++ci) {
+    // the block's chunks: gradient tiles (k_sgrad, or inside the previous
+    // chunk's contraction launch with two gradient buffers), contractions
+    const int64_t nch = cdiv(V, P.chunk_v);
+    auto sgrad_args = [&](int64_t ci) {
+      const int64_t v0 = ci * P.chunk_v;
       const int64_t vrows = std::min<int64_t>(P.chunk_v, V - v0);
-      const int nvt_c = (int)cdiv(vrows, 256);
       SgradArgs sg{};
       sg.St = St + v0 * lds;
       sg.lds = lds;
       sg.lse2 = b.lse2 + t0;
       sg.mask = in.mask ? in.mask + t0 : nullptr;
       sg.scal_f = b.scal_f;
-      sg.G = b.G;
+      sg.G = b.G + (size_t)(ci % P.ngbuf) * P.grows * P.chunk_v;
       sg.vrows = vrows;
       sg.rows = rows;
+      sg.ntt = ntt;
+      sg.nvt = (int)cdiv(vrows, 256);
+      sg.total = sg.ntt * sg.nvt;
       sg.ldg = P.chunk_v;
-      sg.nvt2 = nvt_c * 2;
       sg.c = c;
-      L.run(5, [&] { k_sgrad<<<(unsigned)(ntt * 4 * sg.nvt2), 256, 0, s>>>(sg); });
-      L.run(6, [&] {
-        k_fixup<<<(unsigned)cdiv(rows * K, 256), 256, 0, s>>>(in.idx + t0 * K, b.s + t0 * K, b.pm + t0 * K,
-                                                              b.lse2 + t0, in.mask ? in.mask + t0 : nullptr, b.scal_f,
-                                                              rows, K, v0, vrows, c, b.G, P.chunk_v);
-      });
+      sg.bstart = b.bcnt;
+      sg.bbase = b.bbase;
+      sg.ent = b.ent;
+      sg.ldk = P.ldk;
+      sg.gtt0 = (int)(t0 / 256);
+      sg.gvt0 = (int)(v0 / 256);
+      return sg;
+    };
+    auto pad8 = [](int n) { return (int)(cdiv(n, 8) * 8); };
+    const bool merged = P.ngbuf == 2;
+    {
+      const SgradArgs sg0 = sgrad_args(0);
+      L.run(5, [&] { k_sgrad<<<pad8(sg0.total), 256, 0, s>>>(sg0); });
+    }
+    for (int64_t ci = 0; ci < nch; ++ci) {
+      const int64_t v0 = ci * P.chunk_v;
+      const int64_t vrows = std::min<int64_t>(P.chunk_v, V - v0);
+      const int nvt_c = (int)cdiv(vrows, 256);
       float* dW = nullptr;
       if (dW_out) dW = bf16 ? (whole_dw ? b.dws + v0 * H : b.dws) : static_cast<float*>(dW_out) + v0 * H;
       BwdArgs g{};
       g.W = in.W + v0 * H;
       g.hT = b.hT;
       g.ldt = P.Tb;
-      g.G = b.G;
+      g.G = b.G + (size_t)(ci % P.ngbuf) * P.grows * P.chunk_v;
       g.dH = dH ? dH + t0 * H : nullptr;
       g.dW = dW;
       g.vrows = vrows;
@@ -686,7 +710,18 @@ void launch_seq(Launcher& L, const Plan& P, uint32_t flags, const Inputs& in, co
       g.ldwr = P.ldwr;
       g.acc_dh = ci > 0 || (acc_dh_in && !bf16);
       g.acc_dw = bi > 0 || (acc_dw_in && !bf16);
-      launch_bwd(L, P, g, g.ndh_pad + g.ndw_pad);
+      const int nb = g.ndh_pad + g.ndw_pad;
+      if (ci + 1 < nch && merged) {
+        const SgradArgs sn = sgrad_args(ci + 1);
+        const int s_pad = pad8(sn.total);
+        L.run(11, [&] { k_bwd_sgrad<<<nb + s_pad, 256, 0, s>>>(g, sn, s_pad); });
+      } else {
+        launch_bwd(L, P, g, nb);
+        if (ci + 1 < nch) {
+          const SgradArgs sn = sgrad_args(ci + 1);
+          L.run(5, [&] { k_sgrad<<<pad8(sn.total), 256, 0, s>>>(sn); });
+        }
+      }
       if (dW_out && bf16 && !whole_dw) {
         const int64_t n = vrows * H;
         uint16_t* dst = static_cast<uint16_t*>(dW_out) + v0 * H;

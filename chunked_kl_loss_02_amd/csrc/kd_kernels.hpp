@@ -25,6 +25,11 @@
 //                      dW (over the block's tokens, with h^T from
 //                      k_transpose_h); k_bwd_pass2 runs one unit's
 //                      contractions with the next unit's pass 2.
+//   sequence-chunk schedule: k_pass1<true> also stores a token block's S^T;
+//            k_gather_s reads the logits at the cached ids out of it,
+//            k_sgrad forms the gradient tiles from it (entries in place),
+//            k_bwd_sgrad runs one chunk's contractions with the next
+//            chunk's gradient tiles.
 #pragma once
 #include "kd_gemm.hpp"
 
@@ -546,17 +551,19 @@ __global__ void k_bucket_index(const int32_t* __restrict__ idx, const uint8_t* _
   ent_i[pos] = (uint32_t)i;
 }
 
-// Each placed entry (position p < base[ntt], the number placed) gets its
-// final logit-gradient value bf16(coef * (q - mass)), q = 2^(c s - lse2)
-// from the gathered logit, in place of its slot: t | v << 8 | bits << 16.
-// The same arithmetic as the dense fixup of the sequence-chunk schedule
-// (k_fixup).
+// Each placed entry at a position p in [lo[0], hi[0]) (the whole call:
+// base[0] .. base[ntt], the number placed; one token block: the bases of its
+// first and one-past-last token tiles) gets its final logit-gradient value
+// bf16(coef * (q - mass)), q = 2^(c s - lse2) from the gathered logit, in
+// place of its slot: t | v << 8 | bits << 16.  Both schedules write these
+// entries into their staged gradient tiles (pass 2, or the stored logits'
+// gradient tiles of the sequence-chunk schedule).
 __global__ void k_bucket_value(const float* __restrict__ s, const float* __restrict__ pm,
                                const float* __restrict__ lse2, const float* __restrict__ scal_f, int K, float c,
-                               const uint32_t* __restrict__ total, const uint32_t* __restrict__ ent_i,
-                               uint32_t* __restrict__ ent) {
-  const int64_t p = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-  if (p >= (int64_t)total[0]) return;
+                               const uint32_t* __restrict__ lo, const uint32_t* __restrict__ hi,
+                               const uint32_t* __restrict__ ent_i, uint32_t* __restrict__ ent) {
+  const int64_t p = (int64_t)lo[0] + blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (p >= (int64_t)hi[0]) return;
   const uint32_t i = ent_i[p];
   const uint32_t t = i / (uint32_t)K;
   const float q = fast_exp2(fmaf(s[i], c, -lse2[t]));
@@ -710,25 +717,6 @@ __global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 
   pass2_tile(a, id, st);
 }
 
-// At each cached teacher id inside this (block, chunk), replace the dense
-// value by coef * (q - mass) with q = 2^(c s - lse2) from the gathered logit
-// (the sequence-chunk schedule; the recompute schedule's pass 2 writes the
-// bucketed entries itself).
-__global__ void k_fixup(const int32_t* __restrict__ idx, const float* __restrict__ s, const float* __restrict__ pm,
-                        const float* __restrict__ lse2, const uint8_t* __restrict__ mask,
-                        const float* __restrict__ scal_f, int64_t rows, int K, int64_t v0, int64_t vrows, float c,
-                        uint16_t* __restrict__ G, int ldg) {
-  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-  if (i >= rows * K) return;
-  const int64_t t = i / K;
-  if (mask && mask[t] == 0) return;
-  const int64_t v = (int64_t)idx[i] - v0;
-  if (v < 0 || v >= vrows) return;
-  const float q = fast_exp2(fmaf(s[i], c, -lse2[t]));
-  const float g = scal_f[0] * (q - pm[i]);
-  G[t * ldg + v] = __builtin_bit_cast(uint16_t, (__bf16)g);
-}
-
 // Sequence-chunk schedule: s[t,k] = S[t, idx[t,k]] read from the stored
 // S^T of the block (0 on masked rows), instead of k_gather's dot products.
 __global__ void k_gather_s(const float* __restrict__ St, int64_t lds, const int32_t* __restrict__ idx,
@@ -742,62 +730,116 @@ __global__ void k_gather_s(const float* __restrict__ St, int64_t lds, const int3
   s_out[i] = keep ? St[(int64_t)v * lds + t] : 0.f;
 }
 
-// Sequence-chunk schedule: the logit gradient of one (block, chunk) from the
-// stored S^T, G[t, v - v0] = coef_t 2^(c S[v,t] - lse2[t]) in bf16, zero for
-// masked / padding tokens and vocabulary rows past V; the whole padded tile
-// grid of the chunk is written, as k_pass2 does.  A workgroup transposes a
-// 128 (vocabulary) x 64 (token) tile through LDS: coalesced fp32 reads along
-// tokens, coalesced bf16 writes along the vocabulary.  LDS rows are 65 words
-// (one bank of skew per token row) so both LDS phases are conflict-free.
+// Sequence-chunk schedule: the logit gradient of one (token block,
+// vocabulary chunk) from the block's stored fp32 S^T, one 256 (token) x 256
+// (vocabulary) tile per work id: G = coef * 2^(c S - lse2) on kept tokens,
+// the tile's bucketed teacher entries written in place, bf16.  HBM-bound:
+// 256 KiB read and 128 KiB written per tile.
 struct SgradArgs {
-  const float* St;        // block's S^T, row v0 origin: [*, lds]
+  const float* St;        // block's S^T, chunk origin (row v0): [*, lds]
   int64_t lds;
   const float* lse2;      // block origin
   const uint8_t* mask;    // block origin (nullable)
   const float* scal_f;
-  uint16_t* G;            // [*, ldg]
+  uint16_t* G;            // [ntt * 256, ldg]
   int64_t vrows, rows;    // valid vocabulary rows in the chunk / tokens in the block
-  int ldg, nvt2;          // nvt2 = vocabulary tiles of 128 in the padded chunk
+  int ntt, nvt, total, ldg;
   float c;
+  // teacher entries by tile (k_bucket_*): bucket starts [*, ldk], token-tile
+  // bases, entries; global index of the block's first token tile and of the
+  // chunk's first vocabulary tile
+  const uint32_t* bstart;
+  const uint32_t* bbase;
+  const uint32_t* ent;
+  int ldk, gtt0, gvt0;
 };
 
-__global__ void __launch_bounds__(256) k_sgrad(SgradArgs a) {
-  __shared__ uint32_t tile[64 * 65];
-  const int vt = blockIdx.x % a.nvt2, ttile = blockIdx.x / a.nvt2;
+// One tile, work id `id` < a.total, staged in the four LDS stages (free in
+// either kernel that runs it) as pass 2 stages its tile: [256 tokens][256
+// vocabulary] bf16 rows, 16-byte chunk c of row t at position c ^ (t & 31).
+// The tile's S^T is read 64 tokens at a time (256 rows x 256 bytes), the
+// next group's loads issued before the current group's exponentials; a
+// thread takes 4 tokens of 8 pairs of vocabulary rows and writes the pairs
+// packed.
+__device__ __forceinline__ void sgrad_tile(const SgradArgs& a, int id, Stages st) {
+  const int tt = id / a.nvt, vt = id - tt * a.nvt;
   const int th = threadIdx.x;
-  const int q = th & 15;               // 4 tokens: 4q .. 4q+3
-  const int64_t t0 = (int64_t)ttile * 64;
+  const int q = th & 15, rp = th >> 4;  // tokens 4q .. 4q+3 of a group; pairs rp + 16 j
+  auto row = [&](int tl) -> uint16_t* {
+    uint16_t* b = tl < 64 ? st.a0 : tl < 128 ? st.a1 : tl < 192 ? st.b0 : st.b1;
+    return b + (tl & 63) * 256;
+  };
   const float cf = a.scal_f[0];
-  float l2[4];
-  bool tv[4];
+  const int64_t tb = (int64_t)tt * 256;   // first token of the tile in the block
+  const int64_t vb = (int64_t)vt * 256;   // first vocabulary row of the tile in the chunk
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.St + vb * a.lds, (uint64_t)max<int64_t>(0, min<int64_t>(256, a.vrows - vb)) * (uint64_t)a.lds * 4u);
+  // this tile's teacher entries: [e0, e1) of a.ent
+  const int gtt = a.gtt0 + tt;
+  const int64_t key = (int64_t)gtt * a.ldk + a.gvt0 + vt;
+  const uint32_t bb = a.bbase[gtt];
+  const uint32_t e0 = bb + a.bstart[key], e1 = bb + a.bstart[key + 1];
+  f32x4 x[2][16];
+  auto load = [&](int g, f32x4 (&dst)[16]) {
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int64_t t = t0 + 4 * q + k;
-    tv[k] = t < a.rows && (a.mask ? a.mask[t] != 0 : true);
-    l2[k] = tv[k] ? a.lse2[t] : 0.f;
-  }
+    for (int j = 0; j < 8; ++j)
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int pr = (th >> 4) + 16 * r;  // row pair 0..63: vocabulary rows 2pr, 2pr+1
-    const int64_t v = (int64_t)vt * 128 + 2 * pr;
-    typedef float f32x4 __attribute__((ext_vector_type(4)));
-    f32x4 x0 = {0.f, 0.f, 0.f, 0.f}, x1 = x0;
-    if (v < a.vrows) x0 = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(a.St + v * a.lds + t0) + q);
-    if (v + 1 < a.vrows) x1 = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(a.St + (v + 1) * a.lds + t0) + q);
-    const float s0[4] = {x0[0], x0[1], x0[2], x0[3]}, s1[4] = {x1[0], x1[1], x1[2], x1[3]};
+      for (int r = 0; r < 2; ++r) {
+        const int v = 2 * (rp + 16 * j) + r;  // vocabulary row in the tile (rows past vrows read as zero)
+        const uint32_t off = ((uint32_t)v * (uint32_t)a.lds + (uint32_t)(tb + 64 * g + 4 * q)) * 4u;
+        dst[2 * j + r] = __builtin_bit_cast(f32x4, buf_load16(rs, off));
+      }
+  };
+  load(0, x[0]);
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    if (g < 3) load(g + 1, x[(g + 1) & 1]);
+    float l2[4];
+    bool keep[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const float g0 = tv[k] && v < a.vrows ? cf * fast_exp2(fmaf(s0[k], a.c, -l2[k])) : 0.f;
-      const float g1 = tv[k] && v + 1 < a.vrows ? cf * fast_exp2(fmaf(s1[k], a.c, -l2[k])) : 0.f;
-      tile[(4 * q + k) * 65 + pr] = pack_bf16x2(g0, g1);
+      const int64_t t = tb + 64 * g + 4 * q + k;
+      keep[k] = t < a.rows && (a.mask ? a.mask[t] != 0 : true);
+      l2[k] = keep[k] ? a.lse2[t] : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int pi = rp + 16 * j;  // pair: vocabulary rows 2 pi, 2 pi + 1 of the tile
+      const bool v0ok = vb + 2 * pi < a.vrows, v1ok = vb + 2 * pi + 1 < a.vrows;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int tl = 64 * g + 4 * q + k;
+        const float g0 = keep[k] && v0ok ? cf * fast_exp2(fmaf(x[g & 1][2 * j][k], a.c, -l2[k])) : 0.f;
+        const float g1 = keep[k] && v1ok ? cf * fast_exp2(fmaf(x[g & 1][2 * j + 1][k], a.c, -l2[k])) : 0.f;
+        const int pos = ((((pi >> 2) ^ (tl & 31)) << 2) | (pi & 3)) * 2;  // bf16 offset of the pair
+        *reinterpret_cast<uint32_t*>(row(tl) + pos) = pack_bf16x2(g0, g1);
+      }
     }
   }
   __syncthreads();
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int tl = (th >> 6) + 4 * r, wd = th & 63;
-    reinterpret_cast<uint32_t*>(a.G + (t0 + tl) * a.ldg + (int64_t)vt * 128)[wd] = tile[tl * 65 + wd];
+  // the teacher entries replace the dense values at their (token, id)
+  if (e1 > e0) {
+    for (uint32_t e = e0 + (uint32_t)th; e < e1; e += 256) {
+      const uint32_t xe = a.ent[e];
+      const int tl = xe & 255, vr = (xe >> 8) & 255;
+      row(tl)[((vr >> 3) ^ (tl & 31)) * 8 + (vr & 7)] = (uint16_t)(xe >> 16);
+    }
+    __syncthreads();
   }
+#pragma unroll 4
+  for (int e = th; e < 256 * 32; e += 256) {
+    const int tl = e >> 5, c = e & 31;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(row(tl) + ((c ^ (tl & 31)) * 8));
+    *reinterpret_cast<u32x4*>(a.G + (tb + tl) * a.ldg + vb + c * 8) = v;
+  }
+}
+
+// The tiles of one (block, chunk) alone (the first chunk of a block, and
+// every chunk in the one-gradient-buffer plan).  Grid: total padded to 8.
+__global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) k_sgrad(SgradArgs a) {
+  KD_DECLARE_STAGES(st, 256, 256);
+  const int id = xcd_remap(blockIdx.x, gridDim.x);
+  if (id >= a.total) return;
+  sgrad_tile(a, id, st);
 }
 
 // h^T of one token block: hT[m, t] = h[t0 + t, m] for t < rows, zero for
@@ -1006,6 +1048,27 @@ k_bwd_pass2(BwdArgs g, Pass2Args p, int p_pad) {
   } else {
     const int id = xcd_remap((int)blockIdx.x - nb, p_pad);
     if (id < p.total) pass2_tile(p, id, st);
+  }
+}
+
+// Sequence-chunk schedule: the contractions of one chunk of a token block and
+// the gradient tiles of the block's next chunk, into the other gradient
+// buffer, in one launch.  Grid: the dH work (ndh_pad ids), then the gradient
+// tiles (s_pad, a multiple of 8), then the dW work (ndw_pad).  The long dH
+// tiles fill 3/4 of the CUs; the HBM-bound gradient tiles stream on the rest
+// beside them (a few CUs get far more bandwidth each than all CUs at once),
+// and the dW tiles follow.
+__global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
+k_bwd_sgrad(BwdArgs g, SgradArgs sg, int s_pad) {
+  KD_DECLARE_STAGES(st, 256, 256);
+  const int L = blockIdx.x;
+  if (L < g.ndh_pad) {
+    bwd_tile(g, L, st);
+  } else if (L < g.ndh_pad + s_pad) {
+    const int id = xcd_remap(L - g.ndh_pad, s_pad);
+    if (id < sg.total) sgrad_tile(sg, id, st);
+  } else {
+    bwd_tile(g, L - s_pad, st);
   }
 }
 

@@ -175,13 +175,15 @@ def test_split_entry_point_sizes():
     assert _size(L.kd_topk_kl_workspace_size, T, H, V, K,
                  flags=kd.KD_FLAG_ACCUMULATE_DH | kd.KD_FLAG_ACCUMULATE_DW) == (0, full)
     assert _size(L.kd_topk_kl_workspace_size, T, H, V, K, flags=32)[0] == 1
-    # the sequence-chunk schedule keeps one token block of fp32 logits (block 4096 by default),
-    # one gradient buffer, and defaults to vocabulary chunks of 16384 (12288 otherwise)
+    # the sequence-chunk schedule keeps one token block of fp32 logits (block 4096 by default)
+    # and two gradient buffers (one chunk's contractions run beside the next chunk's gradient
+    # tiles), of vocabulary chunks of 16384 by default (12288 otherwise)
     code, sq = _size(L.kd_topk_kl_workspace_size, T, H, V, K, flags=kd.KD_FLAG_SEQ_CHUNK)
-    assert code == 0 and sq - full == 4 * V * 4096 + 4096 * 16384 * 2 - 2 * 4096 * 12288 * 2
+    assert code == 0 and sq - full == 4 * V * 4096 + 2 * 4096 * 16384 * 2 - 2 * 4096 * 12288 * 2
+    # at equal tiling both schedules keep two gradient buffers: they differ by the block's logits
     assert _size(L.kd_topk_kl_workspace_size, T, H, V, K, flags=kd.KD_FLAG_SEQ_CHUNK, block_t=1024,
                  chunk_v=12288)[1] - _size(L.kd_topk_kl_workspace_size, T, H, V, K, block_t=1024)[1] == \
-        4 * V * 1024 - 1024 * 12288 * 2
+        4 * V * 1024
     for fn in (L.kd_topk_kl_saved_size, L.kd_topk_kl_fwd_workspace_size):
         assert _size(fn, T, 2900, V, K)[0] == 2
 
@@ -271,7 +273,9 @@ def test_tiling_query_reports_the_default_plan():
     assert kd.tiling(1000, 2880, 201088, 64) == (1024, 12288, 2)
     # a single (block, chunk) unit needs one buffer
     assert kd.tiling(1000, 256, 4096, 32, chunk_v=4096) == (1024, 4096, 1)
-    # the sequence-chunk schedule: blocks of 4096, chunks of 16384, one buffer
-    assert kd.tiling(16384, 2880, 201088, 64, seq_chunk=True) == (4096, 16384, 1)
+    # the sequence-chunk schedule: blocks of 4096, chunks of 16384, two buffers when a block has
+    # several chunks, one when the vocabulary is a single chunk
+    assert kd.tiling(16384, 2880, 201088, 64, seq_chunk=True) == (4096, 16384, 2)
+    assert kd.tiling(16384, 256, 16384, 32, seq_chunk=True) == (4096, 16384, 1)
     # the caller's tiling wins
     assert kd.tiling(16384, 2880, 201088, 64, chunk_v=4096, block_t=2048) == (2048, 4096, 2)

@@ -120,6 +120,17 @@ def test_wide_hidden_sizes():
         check(got, ref)
 
 
+@pytest.mark.parametrize("H", [320, 384, 448])
+def test_short_last_hidden_tile(H):
+    # the contractions' last hidden tile is 64 rows high at H % 256 = 64 (320), 128 rows at
+    # H % 256 = 128 (384; its dH tiles read a copy of W's last columns), a full 256-row tile
+    # with rows past H at H % 256 = 192 (448); 3 token blocks x 3 chunks, so dH adds over
+    # chunks and dW over blocks in every form
+    x = make(600, H, 2900, 16, 40 + H % 7, mask="packed8")
+    got, ref = run_case(x, 1.3, chunk_v=1024, block_t=256)
+    check(got, ref)
+
+
 def test_one_k_step_contractions():
     # H = 64: the pass GEMMs run a single k-step (their K loop is H / 64), and
     # with 64 vocabulary rows in the last chunk and 64 tokens so do the

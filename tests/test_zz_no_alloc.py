@@ -66,6 +66,15 @@ def test_noalloc_equals_workspace_entry_point_on_calls_in_a_row():
     run_pair(*to_dev(x3), 1.0, chunk_v=1024, seq_chunk=True)
 
 
+@pytest.mark.parametrize("H", [320, 384])
+def test_short_last_hidden_tile_equals_the_full_height_tile(H):
+    # the workspace entry point computes the last hidden tile 64 (H = 320) or 128 (H = 384)
+    # rows high, the allocation-free one at the full 256 rows: the same dot products in the
+    # same k order, so bitwise the same outputs (several blocks and chunks, accumulation in both)
+    x = synth.make_inputs_np(700, H, 3000, 16, seed=35, mask="packed8")
+    run_pair(*to_dev(x), 0.9, chunk_v=1024, block_t=256)
+
+
 def test_noalloc_gpt_oss_head_with_8192_row_chunks():
     # the documented fit: T 4096, H 2880, V 201088, K 64 at chunk_v 8192
     x = synth.make_inputs_torch(4096, 2880, 201088, 64, seed=2)
