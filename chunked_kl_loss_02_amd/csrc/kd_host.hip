@@ -988,6 +988,12 @@ kd_status kd_topk_kl_fwd(const kd_problem* p, const uint16_t* h, const uint16_t*
 kd_status kd_topk_kl_bwd(const kd_problem* p, const uint16_t* h, const uint16_t* W, const int32_t* teacher_idx,
                          const float* teacher_logit, const uint8_t* mask, const void* saved, const float* grad_loss,
                          void* dH, void* dW, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!p) return KD_ERR_ARG;
+  // the split backward always recomputes: the sequence-chunk flag, which
+  // would change the default tiling, is ignored
+  kd_problem q = *p;
+  q.flags &= ~KD_FLAG_SEQ_CHUNK;
+  p = &q;
   kd_status st = check_common(p, h, W, teacher_idx, teacher_logit, workspace);
   if (st != KD_OK) return st;
   if (!saved) return KD_ERR_ARG;

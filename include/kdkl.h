@@ -84,7 +84,8 @@ typedef enum kd_status {
  * forms the logit gradient from them instead of recomputing the projection:
  * 6 T H V instead of 8 T H V flops, for block_t * V * 4 bytes of workspace
  * (block_t = 0 means 4096 here).  Same results up to fp32 rounding order.
- * kd_topk_kl_fwd / kd_topk_kl_bwd ignore it. */
+ * kd_topk_kl_fwd / kd_topk_kl_bwd ignore it (size their workspaces without
+ * it). */
 #define KD_FLAG_SEQ_CHUNK 16u
 
 typedef struct kd_problem {

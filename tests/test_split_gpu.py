@@ -63,6 +63,29 @@ def test_split_equals_fused_bitwise():
     assert np.max(np.abs(kd.saved_lse(saved, T).cpu().double().numpy() - ref["lse"])) <= 1e-3
 
 
+def test_split_backward_ignores_the_sequence_chunk_flag():
+    # through the C ABI: kd_topk_kl_bwd with KD_FLAG_SEQ_CHUNK set equals the call without it,
+    # bit for bit, with a workspace sized for the problem without the flag
+    print("[split] bwd with the sequence-chunk flag", flush=True)
+    import ctypes
+    x, (h, W, idx, lg, m) = inputs(**CASE)
+    T, H, V, K = CASE["T"], CASE["H"], CASE["V"], CASE["K"]
+    _, saved = kd.fwd(h, W, idx, lg, m, TAU, **KW)
+    dH0, dW0 = kd.bwd(saved, h, W, idx, lg, m, TAU, **KW)
+    p = kd.problem(T, H, V, K, TAU, KW["chunk_v"], KW["block_t"], flags=kd.KD_FLAG_SEQ_CHUNK)
+    ws = torch.empty(kd.workspace_size(T, H, V, K, TAU, **KW), dtype=torch.uint8, device="cuda")
+    dH1 = torch.empty_like(dH0)
+    dW1 = torch.empty_like(dW0)
+    ptr = lambda t: ctypes.c_void_p(t.data_ptr())
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    code = kd.lib().kd_topk_kl_bwd(ctypes.byref(p), ptr(h), ptr(W), ptr(idx), ptr(lg), ptr(m), ptr(saved),
+                                   ctypes.c_void_p(0), ptr(dH1), ptr(dW1), ptr(ws), ctypes.c_size_t(ws.numel()),
+                                   stream)
+    torch.cuda.synchronize()
+    assert code == 0
+    assert torch.equal(dH0, dH1) and torch.equal(dW0, dW1)
+
+
 @pytest.mark.parametrize("g", [-2.5, 0.0, 1e-3])
 def test_incoming_gradient_scales_the_backward(g):
     print(f"[split] grad_loss = {g}", flush=True)
