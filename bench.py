@@ -131,6 +131,28 @@ def merged_flops(T, H, V, K, tau):
     return f, len(units) - 1
 
 
+def kernel_flops(T, H, V, K, tau):
+    """MFMA flops per call of each GEMM kernel class of the recompute
+    schedule, from the library's (token block, vocabulary chunk) units:
+    pass 1 computes every logit once (2 H per logit); with two gradient
+    buffers the first unit's pass 2 runs alone (pass2), the merged launches
+    hold the rest (bwd_pass2, see merged_flops) and the last unit's
+    contractions run alone (bwd); with one buffer every unit's pass 2 and
+    contractions run as pass2 and bwd."""
+    import chunked_kl_loss_02_amd as kd
+    bt, cv, nbuf = kd.tiling(T, H, V, K, tau)
+    units = [(min(bt, T - t0), min(cv, V - v0)) for t0 in range(0, T, bt) for v0 in range(0, V, cv)]
+    out = {"pass1": 2.0 * T * H * V}
+    if nbuf < 2:
+        out["pass2"] = sum(2.0 * H * r * v for r, v in units)
+        out["bwd"] = sum(4.0 * H * r * v for r, v in units)
+    else:
+        out["pass2"] = 2.0 * H * units[0][0] * units[0][1]
+        out["bwd"] = 4.0 * H * units[-1][0] * units[-1][1]
+        out["bwd_pass2"] = merged_flops(T, H, V, K, tau)[0]
+    return out
+
+
 def run_seq_chunk(args, wl, x):
     """The sequence-chunk schedule on the same inputs: pass 1 keeps a token
     block's logits (fp32, in the workspace) and the gradient is formed from
@@ -301,6 +323,10 @@ def run_one(args, wl):
         "tflops_total": flops_per_token(H, V) * T * args.steps / dt / 1e12,
         "mfma_util_total": flops_per_token(H, V) * T * args.steps / dt / 1e12 / PEAK_BF16_TFLOPS,
         "per_kernel_ms_per_step": {k: v[0] / args.steps for k, v in per_kernel.items() if v[1]},
+        # MFMA rate of each GEMM kernel class over its event-timed share of a step
+        "per_kernel_tflops": {k: f * args.steps / (per_kernel[k][0] * 1e-3) / 1e12
+                              for k, f in kernel_flops(T, H, V, K, tau).items()
+                              if k in per_kernel and per_kernel[k][1] and per_kernel[k][0] > 0},
         "ms_per_step_all_events": dt_all * 1e3 / args.steps,
         "peak_mem_bytes": int(peak),
         "peak_mem_inputs_outputs_workspace_bytes": int(base_alloc),
