@@ -136,6 +136,12 @@ def test_long_context_restricted_mask_full_grads():
     protocol_ii(synth.WORKLOADS["long"])
 
 
+def test_long_context_seq_chunk_restricted_mask_full_grads():
+    # the sequence-chunk schedule: dW summed over 8 token blocks of 4096, each block's chunks
+    # formed from its stored logits beside the previous chunk's contractions
+    protocol_ii(synth.WORKLOADS["long"], seq_chunk=True)
+
+
 def test_pages_k100_head():
     # the pages cache the teacher's top-100 per position
     protocol_ii(synth.Workload("k100", 1024, 2880, 201088, 100, 1.0), n_rows=64)
