@@ -25,7 +25,8 @@
  * Memory: besides the caller's inputs and outputs the library touches only
  * the caller's workspace (see kd_topk_kl_workspace_size): two fixed
  * block_t x chunk_v bf16 gradient buffers (one when the call has a single
- * token block and vocabulary chunk), h^T of one token block (H x block_t
+ * token block and vocabulary chunk, or with KD_FLAG_SEQ_CHUNK a single
+ * vocabulary chunk), h^T of one token block (H x block_t
  * bf16), when H % 256 is 64 or 128 a copy of W's last H % 256 columns
  * ((H % 256) x V bf16, rounded up to 64 columns of V), plus
  * O(T*K + T*V/256) per-token state.  It allocates no device
