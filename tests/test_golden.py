@@ -21,3 +21,14 @@ def test_flops_per_token():
     # pass-1 GEMM, pass-2 recompute, dH and dW: 2*H*V each
     assert bench.flops_per_token(2880, 201088) == 8 * 2880 * 201088
     assert abs(bench.flops_per_token(2880, 201088) / 1e9 - 4.633) < 1e-3
+
+
+def test_per_kernel_flops_add_up_to_the_step():
+    # the bench's per-kernel MFMA rates split 8 T H V over the library's own units: pass 1,
+    # the first unit's pass 2, the merged launches, the last unit's contractions (or, with one
+    # gradient buffer, every unit's pass 2 and contractions)
+    for T, H, V, K, kw in ((4096, 2880, 201088, 64, {}), (16384, 2880, 201088, 64, {}),
+                          (1000, 256, 4096, 32, {}), (700, 128, 3000, 16, {})):
+        f = bench.kernel_flops(T, H, V, K, 1.0)
+        assert abs(sum(f.values()) - 8.0 * T * H * V) <= 1e-9 * 8.0 * T * H * V, (T, f)
+        assert f["pass1"] == 2.0 * T * H * V
