@@ -27,8 +27,8 @@ def test_per_kernel_flops_add_up_to_the_step():
     # the bench's per-kernel MFMA rates split 8 T H V over the library's own units: pass 1,
     # the first unit's pass 2, the merged launches, the last unit's contractions (or, with one
     # gradient buffer, every unit's pass 2 and contractions)
-    for T, H, V, K, kw in ((4096, 2880, 201088, 64, {}), (16384, 2880, 201088, 64, {}),
-                          (1000, 256, 4096, 32, {}), (700, 128, 3000, 16, {})):
+    for T, H, V, K in ((4096, 2880, 201088, 64), (16384, 2880, 201088, 64), (1000, 256, 4096, 32),
+                       (700, 128, 3000, 16)):
         f = bench.kernel_flops(T, H, V, K, 1.0)
         assert abs(sum(f.values()) - 8.0 * T * H * V) <= 1e-9 * 8.0 * T * H * V, (T, f)
         assert f["pass1"] == 2.0 * T * H * V
