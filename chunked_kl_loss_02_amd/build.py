@@ -13,8 +13,6 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkdkl.so")
 SOURCES = [os.path.join(CSRC, "kd_host.hip")]
-DEPS = SOURCES + [os.path.join(CSRC, f) for f in ("kd_common.hpp", "kd_gemm.hpp", "kd_kernels.hpp")] + [
-    os.path.join(os.path.dirname(HERE), "include", "kdkl.h")]
 
 ARCH = "gfx950"
 
