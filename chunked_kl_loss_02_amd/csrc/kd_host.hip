@@ -111,6 +111,9 @@ kd_status check(const kd_problem* p) {
   const int64_t lim = (int64_t)UINT32_MAX;
   if (cv * p->H * 4 > lim || bt * p->H * 4 > lim || bt * cv * 2 > lim) return KD_ERR_UNSUPPORTED;
   if (256 * p->H * 2 > lim / 2) return KD_ERR_UNSUPPORTED;
+  // the sequence-chunk schedule's gradient tiles read 256 stored fp32 logit
+  // rows of one token block (bt columns each) through one 32-bit range
+  if ((p->flags & KD_FLAG_SEQ_CHUNK) && 256 * bt * 4 > lim) return KD_ERR_UNSUPPORTED;
   return KD_OK;
 }
 

@@ -718,7 +718,8 @@ __global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 
 }
 
 // Sequence-chunk schedule: s[t,k] = S[t, idx[t,k]] read from the stored
-// S^T of the block (0 on masked rows), instead of k_gather's dot products.
+// S^T of the block (0 on masked rows); the recompute schedule reads them out
+// of pass 1's tiles instead (gather_tile_t).
 __global__ void k_gather_s(const float* __restrict__ St, int64_t lds, const int32_t* __restrict__ idx,
                            const uint8_t* __restrict__ mask, int64_t rows, int K, int64_t V,
                            float* __restrict__ s_out) {

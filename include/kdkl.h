@@ -50,7 +50,8 @@ typedef enum kd_status {
   KD_ERR_UNSUPPORTED = 2,  /* valid but not supported: H % 64 != 0, K > 1024, bad alignment,
                               chunk_v / block_t not multiples of 256, or one chunk or block
                               too large for 32-bit offsets: chunk_v * H * 4, block_t * H * 4
-                              and block_t * chunk_v * 2 must each be below 4 GiB (the chunk
+                              and block_t * chunk_v * 2 must each be below 4 GiB, and
+                              256 * block_t * 4 too with KD_FLAG_SEQ_CHUNK (the chunk
                               and block actually used, defaults included) */
   KD_ERR_WORKSPACE = 3,    /* workspace_bytes smaller than kd_topk_kl_workspace_size() */
   KD_ERR_INDEX = 4,        /* (KD_FLAG_VALIDATE) a kept row has a teacher id outside [0, V) */

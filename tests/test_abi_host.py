@@ -111,6 +111,19 @@ def test_fp32_gradient_targets_must_fit_32_bit_offsets():
     assert _size(L.kd_topk_kl_fwd_workspace_size, 512, 5120, 262144, 64, chunk_v=262144, block_t=256)[0] == 2
 
 
+def test_stored_logit_rows_of_a_block_must_fit_32_bit_offsets():
+    """The sequence-chunk schedule's gradient tiles read 256 stored fp32
+    logit rows of a token block (one column per token) through one 32-bit
+    buffer range, so 256 * block * 4 bytes must stay below 4 GiB."""
+    def ws(block_t, flags):
+        p = kd.problem(block_t, 64, 1000, 1, 1.0, 256, block_t, flags=flags)
+        n = ctypes.c_size_t(0)
+        return kd.lib().kd_topk_kl_workspace_size(ctypes.byref(p), ctypes.byref(n))
+    assert ws(4194304, kd.KD_FLAG_SEQ_CHUNK) == 2          # exactly 4 GiB
+    assert ws(4194304 - 256, kd.KD_FLAG_SEQ_CHUNK) == 0
+    assert ws(4194304, 0) == 0                             # the recompute schedule stores none
+
+
 def test_fwd_bwd_rejects_bad_arguments_before_any_hip_call():
     L = kd.lib()
     vp = ctypes.c_void_p

@@ -112,8 +112,9 @@ def test_realistic_hidden_size():
 
 
 def test_wide_hidden_sizes():
-    # the teacher-id gather holds h rows of up to 8192 in registers (H = 4160
-    # and 8192 there) and loops over longer rows (H = 8256)
+    # long K loops in the pass GEMMs (65, 128 and 129 k-steps of 64) and 17-33
+    # hidden tiles in the contractions, the last one 64 rows high at H = 4160
+    # and 8256 (H % 256 = 64), full at H = 8192
     for T, H, seed in ((40, 4160, 11), (24, 8192, 12), (24, 8256, 13)):
         x = make(T, H, 700, 8, seed)
         got, ref = run_case(x, 1.0)
