@@ -28,7 +28,7 @@ KD_FLAG_SEQ_CHUNK = 16
 ABI_VERSION = 5
 KD_FLAG_LOGITS_F32 = 32
 NOALLOC_SCRATCH_BYTES = 128 << 20  # KD_NOALLOC_SCRATCH_BYTES
-KERNEL_CLASSES = ("teacher", "gather", "pass1", "lse", "loss", "pass2", "fixup", "bwd", "other", "logits", "topk",
+KERNEL_CLASSES = ("teacher", "gather", "pass1", "lse", "loss", "pass2", "buckets", "bwd", "other", "logits", "topk",
                   "bwd_pass2")
 _STATUS = {0: "KD_OK", 1: "KD_ERR_ARG", 2: "KD_ERR_UNSUPPORTED", 3: "KD_ERR_WORKSPACE",
            4: "KD_ERR_INDEX", 5: "KD_ERR_NONFINITE", 6: "KD_ERR_HIP"}

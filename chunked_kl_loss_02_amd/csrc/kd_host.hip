@@ -98,9 +98,11 @@ kd_status check(const kd_problem* p) {
   if (p->H % 64 != 0) return KD_ERR_UNSUPPORTED;
   if (p->K > kd::kTeacherMaxK) return KD_ERR_UNSUPPORTED;
   if (p->chunk_v % 256 != 0 || p->block_t % 256 != 0) return KD_ERR_UNSUPPORTED;
-  if (p->V > (int64_t)INT32_MAX || p->T > ((int64_t)1 << 40)) return KD_ERR_UNSUPPORTED;
-  // 32-bit positions of the bucketed teacher entries
-  if (p->T * (int64_t)p->K > (int64_t)UINT32_MAX) return KD_ERR_UNSUPPORTED;
+  // Launch grids stay under 2^32 work-items (the limit of a dispatch): 64
+  // per token in k_teacher, one per teacher entry in the bucket kernels
+  // (whose positions are 32-bit too), and pass 1 below.
+  if (p->V > (int64_t)INT32_MAX || p->T > ((int64_t)1 << 26) - 256) return KD_ERR_UNSUPPORTED;
+  if (p->T * (int64_t)p->K > (int64_t)UINT32_MAX - 255) return KD_ERR_UNSUPPORTED;
   // Every kernel addresses one chunk or block operand through 32-bit buffer
   // offsets: the bf16 chunk of W and the token block of h (and its h^T), the
   // bf16 gradient buffer (block x chunk), and the fp32 gradient targets the
@@ -114,6 +116,8 @@ kd_status check(const kd_problem* p) {
   // the sequence-chunk schedule's gradient tiles read 256 stored fp32 logit
   // rows of one token block (bt columns each) through one 32-bit range
   if ((p->flags & KD_FLAG_SEQ_CHUNK) && 256 * bt * 4 > lim) return KD_ERR_UNSUPPORTED;
+  // pass 1: 256 work-items per (token tile, vocabulary tile) of one block
+  if (cdiv(cdiv(bt, 256) * cdiv(p->V, 256), 8) * 8 * 256 > lim) return KD_ERR_UNSUPPORTED;
   return KD_OK;
 }
 
@@ -1037,7 +1041,9 @@ kd_status check_logits(const kd_logits_problem* p) {
   if (!(p->tau > 0.f) || !isfinite(p->tau)) return KD_ERR_ARG;
   if (p->flags & ~(KD_FLAG_VALIDATE | KD_FLAG_LOGITS_F32)) return KD_ERR_ARG;
   if (p->K > kd::kTeacherMaxK) return KD_ERR_UNSUPPORTED;
-  if (p->V > (int64_t)INT32_MAX || p->T > ((int64_t)1 << 40) || p->T > (int64_t)INT32_MAX) return KD_ERR_UNSUPPORTED;
+  // one workgroup of kLrowThreads per row, under 2^32 work-items a launch
+  if (p->V > (int64_t)INT32_MAX || p->T > (int64_t)UINT32_MAX / std::max(kd::kLrowThreads, kd::kLrowRegThreads))
+    return KD_ERR_UNSUPPORTED;
   return KD_OK;
 }
 
@@ -1175,7 +1181,8 @@ kd_status kd_topk_select(const kd_topk_problem* p, const uint16_t* X, int32_t* i
   if (p->T < 0 || p->V <= 0 || p->K <= 0 || (int64_t)p->K > p->V || p->flags != 0) return KD_ERR_ARG;
   if (p->T > 0 && (!X || !idx || !values)) return KD_ERR_ARG;
   using namespace kd;
-  if (p->K > kTopkMaxK || p->V % 8 != 0 || p->V > (int64_t)INT32_MAX / 2 || p->T > (int64_t)INT32_MAX)
+  // one workgroup of kTopkThreads per row, under 2^32 work-items a launch
+  if (p->K > kTopkMaxK || p->V % 8 != 0 || p->V > (int64_t)INT32_MAX / 2 || p->T > (int64_t)UINT32_MAX / kTopkThreads)
     return KD_ERR_UNSUPPORTED;
   if (misaligned(X, 16) || misaligned(idx, 4) || misaligned(values, 4)) return KD_ERR_UNSUPPORTED;
   Launcher L{static_cast<hipStream_t>(stream)};

@@ -52,7 +52,9 @@ typedef enum kd_status {
                               too large for 32-bit offsets: chunk_v * H * 4, block_t * H * 4
                               and block_t * chunk_v * 2 must each be below 4 GiB, and
                               256 * block_t * 4 too with KD_FLAG_SEQ_CHUNK (the chunk
-                              and block actually used, defaults included) */
+                              and block actually used, defaults included); or a launch
+                              grid past 2^32 work-items (the limits on T, T * K and,
+                              for pass 1, (block / 256) * ceil(V / 256) at most 2^24 - 8) */
   KD_ERR_WORKSPACE = 3,    /* workspace_bytes smaller than kd_topk_kl_workspace_size() */
   KD_ERR_INDEX = 4,        /* (KD_FLAG_VALIDATE) a kept row has a teacher id outside [0, V) */
   KD_ERR_NONFINITE = 5,    /* (KD_FLAG_VALIDATE) a kept row has a NaN/+inf logit or all -inf */
@@ -91,7 +93,8 @@ typedef enum kd_status {
 #define KD_FLAG_SEQ_CHUNK 16u
 
 typedef struct kd_problem {
-  int64_t T;        /* tokens (rows of h); 0 allowed (loss = 0, dW = 0) */
+  int64_t T;        /* tokens (rows of h); 0 allowed (loss = 0, dW = 0); at most
+                       2^26 - 256, and T * K at most 2^32 - 256 */
   int64_t H;        /* hidden size; multiple of 64 */
   int64_t V;        /* vocabulary size; >= 1 */
   int32_t K;        /* cached teacher entries per token; 1 <= K <= min(V, 1024) */
@@ -223,7 +226,7 @@ kd_status kd_topk_kl_bwd(const kd_problem* p,
 #define KD_FLAG_LOGITS_F32 32u  /* Z and dZ are fp32 (default: bf16 bit patterns) */
 
 typedef struct kd_logits_problem {
-  int64_t T;        /* rows of Z; 0 allowed (loss = 0) */
+  int64_t T;        /* rows of Z; 0 allowed (loss = 0); below 2^23 */
   int64_t V;        /* vocabulary size; >= 1 */
   int32_t K;        /* cached teacher entries per row; 1 <= K <= min(V, 1024) */
   float tau;        /* temperature; finite, > 0 */
@@ -256,7 +259,7 @@ kd_status kd_topk_kl_logits(const kd_logits_problem* p, const void* Z,
  * No workspace; asynchronous on `stream`.
  */
 typedef struct kd_topk_problem {
-  int64_t T;        /* rows; 0 allowed */
+  int64_t T;        /* rows; 0 allowed; below 2^23 */
   int64_t V;        /* row length */
   int32_t K;        /* entries per row */
   uint32_t flags;   /* must be 0 */
@@ -285,8 +288,8 @@ int kd_abi_version(void);
  * around every launch of the library's kernels while enabled.  Intended for
  * benchmarks; the state is process-wide (calls from several threads add
  * their launches to one list, under a lock).  Kernel classes: 0 teacher, 1 gather,
- * 2 pass1, 3 lse, 4 loss, 5 pass2, 6 fixup (the teacher-entry buckets or
- * the dense fixup), 7 bwd, 8 other, 9 logits (the row kernel of
+ * 2 pass1, 3 lse, 4 loss, 5 pass2, 6 buckets (the teacher entries bucketed
+ * by tile and their gradient values), 7 bwd, 8 other, 9 logits (the row kernel of
  * kd_topk_kl_logits), 10 topk (kd_topk_select), 11 bwd_pass2 (one unit's
  * contractions with the next unit's pass 2).
  * kd_timing_collect synchronises the recorded events, adds each class's

@@ -124,6 +124,29 @@ def test_stored_logit_rows_of_a_block_must_fit_32_bit_offsets():
     assert ws(4194304, 0) == 0                             # the recompute schedule stores none
 
 
+def test_launch_grids_stay_under_2_to_the_32_work_items():
+    """A dispatch holds at most 2^32 - 1 work-items: the per-token teacher
+    kernel (64 per token), the per-entry bucket kernels (one per entry) and
+    pass 1 (256 per token tile x vocabulary tile of a block) bound T, T * K
+    and block * V; a problem past them is refused instead of failing at
+    launch."""
+    assert _ws((1 << 26) - 256, 64, 1000, 1)[0] == 0
+    assert _ws((1 << 26) - 255, 64, 1000, 1)[0] == 2
+    assert _ws(1 << 22, 64, 2048, 1023)[0] == 0            # T K = 2^32 - 2^22
+    assert _ws(1 << 22, 64, 2048, 1024)[0] == 2            # T K = 2^32
+    # pass 1 over 32 token tiles x 2^19 vocabulary tiles (2^24 tiles) ...
+    assert _ws(8192, 64, 1 << 27, 1, 1.0, 0, 8192)[0] == 2
+    # ... or over one token tile: fine
+    assert _ws(256, 64, 1 << 27, 1, 1.0, 0, 256)[0] == 0
+    assert _ws(8192, 64, 1 << 24, 1, 1.0, 0, 8192)[0] == 0
+    L = kd.lib()
+    n = ctypes.c_size_t(0)
+    ok = kd.KdLogitsProblem((1 << 23) - 1, 1000, 4, 1.0, 0)
+    assert L.kd_topk_kl_logits_workspace_size(ctypes.byref(ok), ctypes.byref(n)) == 0
+    big = kd.KdLogitsProblem(1 << 23, 1000, 4, 1.0, 0)
+    assert L.kd_topk_kl_logits_workspace_size(ctypes.byref(big), ctypes.byref(n)) == 2
+
+
 def test_fwd_bwd_rejects_bad_arguments_before_any_hip_call():
     L = kd.lib()
     vp = ctypes.c_void_p
@@ -239,6 +262,7 @@ def test_topk_select_validates_before_any_hip_call():
     assert call(4, 1001, 4) == 2               # V % 8
     assert call(4, 2048, 1025) == 2            # K > 1024
     assert call(4, 1 << 30, 4) == 2            # V past 2^30 - 1
+    assert call(1 << 23, 1000, 4) == 2         # 512 work-items a row: past 2^32
     assert call(4, 1000, 4, X=vp((1 << 20) + 2)) == 2  # misaligned rows
 
 
