@@ -202,7 +202,12 @@ def _check_out(t, shape, dtype, dev, what):
 
 
 def _workspace(workspace, nbytes, dev):
+    """The caller's workspace (a contiguous uint8 tensor on the inputs'
+    device) if it is large enough, else a new one."""
     import torch
+    if workspace is not None and (workspace.dtype != torch.uint8 or workspace.device != dev
+                                  or not workspace.is_contiguous()):
+        raise ValueError(f"workspace must be a contiguous uint8 tensor on {dev}")
     if workspace is None or workspace.numel() < nbytes:
         workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
     return workspace

@@ -316,3 +316,18 @@ def test_tiling_query_reports_the_default_plan():
     assert kd.tiling(16384, 256, 16384, 32, seq_chunk=True) == (4096, 16384, 1)
     # the caller's tiling wins
     assert kd.tiling(16384, 2880, 201088, 64, chunk_v=4096, block_t=2048) == (2048, 4096, 2)
+
+
+def test_binding_refuses_a_workspace_it_cannot_hand_to_the_library():
+    # a workspace on another device, of another dtype or non-contiguous raises
+    # before any call (its address would otherwise reach the kernels)
+    torch = pytest.importorskip("torch")
+    gpu = torch.device("cuda", 0)
+    with pytest.raises(ValueError):
+        kd._workspace(torch.empty(1024, dtype=torch.uint8), 512, gpu)
+    with pytest.raises(ValueError):
+        kd._workspace(torch.empty(1024, dtype=torch.float32), 512, torch.device("cpu"))
+    with pytest.raises(ValueError):
+        kd._workspace(torch.empty(2048, dtype=torch.uint8)[::2], 512, torch.device("cpu"))
+    ws = torch.empty(1024, dtype=torch.uint8)
+    assert kd._workspace(ws, 512, torch.device("cpu")) is ws
