@@ -9,17 +9,19 @@
 //   1. one pass over the row: each thread keeps the two largest keys of its
 //      even-indexed and of its odd-indexed elements, both pairs in the two
 //      16-bit halves of two registers (packed 16-bit min / max, about four
-//      ALU operations per element); theta, the K-th largest of those 2048
+//      ALU operations per element), and the vector where each half's largest
+//      key first appeared; theta, the K-th largest of those 2048
 //      keys, is a lower bound of the row's K-th largest (K distinct elements
 //      reach it), found bit by bit;
-//   2. every (key, id) with key >= theta goes to LDS: the pass also noted
-//      where each half's best key was seen, which is all a thread holds at or
-//      above theta unless its second key reaches theta too; only such
+//   2. every (key, id) with key >= theta goes to LDS: a thread's best key
+//      per half (its position found again in the noted vector) is all it
+//      holds at or above theta unless its second key reaches theta too; only such
 //      threads' shares of the row (one in 512 vectors each) are scanned
 //      again, one share per wave with a vector per lane (for ordinary rows a
 //      few shares);
-//   3. the candidates are sorted in LDS (bitonic: descending key, ascending
-//      id) and the first K written out.
+//   3. the order is descending key, then ascending id: up to 512 candidates
+//      each count the candidates ahead of them and the first K go straight to
+//      their places; larger sets are sorted in LDS (bitonic) first.
 // The pass ranks -0 just below +0 (raw keys); a theta at either zero is
 // lowered to the -0 key, so that every zero is a candidate, and the
 // candidates carry keys on which -0 equals +0.
@@ -132,24 +134,26 @@ __global__ void __launch_bounds__(kTopkThreads) k_topk(TopkArgs a) {
   int rb = 0;
   // 1. per half (even / odd elements): m1 = largest raw key, m2 = second
   uint32_t m1 = 0, m2 = 0;  // key 0 (the pattern 0xFFFF, a NaN) is the floor
-  // word of the thread's share (4 per vector) where each half's m1 was seen
+  // vector of the thread's share (its n-th: row vector tid + 512 n) where
+  // each half's m1 was first seen; the word inside it is found again later
   int p_lo = 0, p_hi = 0;
   constexpr int kAhead = 4;  // vectors in flight per thread
   int pos = 0;
   auto fold = [&](const u32x4 (&v)[kAhead]) {
 #pragma unroll
-    for (int u = 0; u < kAhead; ++u)
+    for (int u = 0; u < kAhead; ++u, ++pos) {
+      const uint32_t before = m1;
 #pragma unroll
-      for (int q = 0; q < 4; ++q, ++pos) {
+      for (int q = 0; q < 4; ++q) {
         const uint32_t k = raw_key2(v[u][q]);
         const uint32_t lo = pk_min_u16(k, m1);
-        const uint32_t n1 = pk_max_u16(k, m1);
-        const uint32_t ch = n1 ^ m1;  // a half changes only for a strictly larger key
-        p_lo = (ch & 0xFFFFu) ? pos : p_lo;
-        p_hi = (ch >> 16) ? pos : p_hi;
-        m1 = n1;
+        m1 = pk_max_u16(k, m1);
         m2 = pk_max_u16(lo, m2);
       }
+      const uint32_t ch = m1 ^ before;  // a half changes only for a strictly larger key
+      p_lo = (ch & 0xFFFFu) ? pos : p_lo;
+      p_hi = (ch >> 16) ? pos : p_hi;
+    }
   };
   const u32x4* rv = reinterpret_cast<const u32x4*>(row);
   int64_t i0 = tid;
@@ -195,11 +199,20 @@ __global__ void __launch_bounds__(kTopkThreads) k_topk(TopkArgs a) {
     for (int hf = 0; hf < 2; ++hf) {
       const uint32_t rk = hf ? (m1 >> 16) : (m1 & 0xFFFFu);
       if (rk >= theta) {
-        const int pw = hf ? p_hi : p_lo;
+        // the vector where the key first appeared: its first word whose half
+        // holds the key (earlier words of the vector hold smaller keys)
+        const int64_t gi = (int64_t)tid + (int64_t)kTopkThreads * (hf ? p_hi : p_lo);
+        const u32x4 v = rv[gi];
+        int q = 3;
+#pragma unroll
+        for (int qq = 2; qq >= 0; --qq) {
+          const uint32_t k = raw_key2(v[qq]);
+          if ((hf ? (k >> 16) : (k & 0xFFFFu)) == rk) q = qq;
+        }
         const int p = atomicAdd(&ncand, 1);
         if (p < kTopkCand) {
           ck[p] = rk == 0x7FFFu ? 0x8000u : rk;  // -0 as +0
-          ci[p] = (int32_t)(8 * ((int64_t)tid + (int64_t)kTopkThreads * (pw >> 2)) + 2 * (pw & 3) + hf);
+          ci[p] = (int32_t)(8 * gi + 2 * q + hf);
         }
       }
     }
@@ -284,6 +297,26 @@ __global__ void __launch_bounds__(kTopkThreads) k_topk(TopkArgs a) {
     }
     __syncthreads();
     ns = K;
+  }
+  if (ns <= kTopkThreads) {
+    // at most one candidate per thread: its place in the order (larger key
+    // first, then smaller id) is the number of candidates ahead of it (all
+    // (key, id) pairs differ), and the first K places are written directly
+    if (tid < ns) {
+      const uint32_t ki = ck[tid];
+      const int32_t ii = ci[tid];
+      int rank = 0;
+      for (int j = 0; j < ns; ++j) {
+        const uint32_t kj = ck[j];
+        const int32_t ij = ci[j];
+        rank += (kj > ki) | ((kj == ki) & (ij < ii));
+      }
+      if (rank < K) {
+        a.idx[t * K + rank] = ii;
+        a.val[t * K + rank] = key_bf16_value(ki);
+      }
+    }
+    return;
   }
   int np = 1;
   while (np < ns) np <<= 1;
