@@ -864,11 +864,12 @@ const char* kd_status_string(kd_status s) {
   switch (s) {
     case KD_OK: return "ok";
     case KD_ERR_ARG: return "invalid argument";
-    case KD_ERR_UNSUPPORTED: return "unsupported problem (H % 64, K > 1024, chunk/block not multiples of 256, size or alignment)";
+    case KD_ERR_UNSUPPORTED: return "unsupported problem (H % 64, K > 1024, chunk/block not multiples of 256, size limits or alignment)";
     case KD_ERR_WORKSPACE: return "workspace too small";
     case KD_ERR_INDEX: return "teacher index out of range";
     case KD_ERR_NONFINITE: return "teacher logits NaN/+inf or all -inf in a kept row";
     case KD_ERR_HIP: return "HIP runtime error";
+    default: break;
   }
   return "unknown status";
 }
